@@ -1,0 +1,222 @@
+/*
+ * libmuon — the Muon optimizer step (momentum orthogonalised by quintic
+ * Newton–Schulz) for the 2-D weight matrices of a GPT-2-style body, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *  [P4] "modded-nanogpt 50B-token 长时程训练实验解析：Muon vs Adam 与数据复用策略的实证对比",
+ *       section "从源码看 Muon 的分布式正交化实现" (Muon's orthogonalisation, from
+ *       the source) and section "超参配置解析" (hyper-parameters).
+ *  [P2] "2025-10-27_FixMuonLR" record analysis, sections "改动一" (per-matrix
+ *       lr_mul / wd_mul, the Muon learning rate) and "改动二" (the vectorised
+ *       step, the lerp momentum buffer owned by the group, reset(), the early
+ *       qkvo reshape, NorMuon's per-lane second moment).
+ *  [P3] "2024-11-19 FlexAttention" record analysis, optimizer section
+ *       (Muon on 2-D params, 5 NS steps, momentum warm-up 0.85 -> 0.95).
+ *
+ * Conventions for every entry point:
+ *  - Plain C: pointers and sizes only. Device pointers are HIP device
+ *    addresses; `stream` is a hipStream_t passed as void* (NULL = the
+ *    default stream of the current device).
+ *  - Ownership: the caller owns params, grads, momentum and the workspace.
+ *    A handle owns only host memory. The library never allocates device
+ *    memory; muon_init uploads its descriptor tables into the caller's
+ *    workspace with a blocking copy; muon_step and muon_reset only enqueue
+ *    work on `stream` and never synchronise.
+ *  - Errors: every call returns a muon_status; nothing aborts or throws
+ *    across the ABI. Validation happens before any HIP call. A kernel fault
+ *    surfaces at the caller's next synchronisation. Handles are not
+ *    thread-safe; use one stream per handle per call.
+ */
+#ifndef LIBMUON_H
+#define LIBMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum muon_status {
+    MUON_OK = 0,
+    MUON_E_INVALID_ARG = -1, /* null pointer, bad enum, non-finite / out-of-range scalar */
+    MUON_E_SHAPE = -2,       /* rows, cols or count < 1 */
+    MUON_E_LAYOUT = -3,      /* negative offset, overlap, extent beyond the buffers */
+    MUON_E_NO_DEVICE = -4,   /* no HIP device, or the device is not gfx950 */
+    MUON_E_HIP = -5,         /* a HIP runtime call failed (see muon_last_error) */
+    MUON_E_STATE = -6,       /* misuse of a handle (wrong device current, ...) */
+    MUON_E_WORKSPACE = -7    /* workspace null, misaligned (256 B) or too small */
+} muon_status;
+
+/* One table entry: `count` contiguous row-major [rows, cols] float32 matrices
+ * starting at element `offset` of the flat params / grads / momentum buffers
+ * (count = 4 expresses the fused qkvo weight as its four [d, d] matrices,
+ * [P2] change 2). Only 2-D weights belong here ([P4] Muon source).
+ * lr_mul / wd_mul scale lr and weight decay for these matrices ([P2] change 1).
+ * frozen != 0: params and momentum of these matrices are never touched. */
+typedef struct muon_matrix {
+    int64_t rows;
+    int64_t cols;
+    int64_t count;
+    int64_t offset;
+    float lr_mul;
+    float wd_mul;
+    int32_t frozen;
+    int32_t reserved; /* must be 0 */
+} muon_matrix;
+
+#define MUON_MAX_NS_STEPS 16
+
+enum { MUON_NS_BF16 = 0, MUON_NS_FP32 = 1 };
+enum { MUON_MOMENTUM_LERP = 0, MUON_MOMENTUM_HEAVY_BALL = 1 };
+
+/* Hyper-parameters ([P4] hyper-parameter and Muon source sections):
+ *  momentum 0.95, nesterov 1, ns_steps 5 with (a, b, c) = (3.4445, -4.7750,
+ *  2.0315) per iteration, ns_eps 1e-7, weight_decay 0, NorMuon off
+ *  (beta2 0.95, eps 1e-10 when on). ns_coeffs[k] holds (a, b, c) of
+ *  iteration k, so a per-iteration schedule can replace the fixed quintic.
+ *  momentum_kind LERP: m <- beta m + (1-beta) g, Nesterov u = (1-beta) g + beta m
+ *  ([P2] change 2); HEAVY_BALL: m <- beta m + g, Nesterov u = g + beta m
+ *  ([P4] Muon source). ns_precision BF16: bf16 MFMA operands with fp32
+ *  accumulation; FP32: fp32 throughout (debug / reference mode). */
+typedef struct muon_hparams {
+    float momentum;
+    int32_t nesterov;
+    int32_t momentum_kind;
+    int32_t ns_steps;
+    float ns_coeffs[MUON_MAX_NS_STEPS][3];
+    float ns_eps;
+    int32_t ns_precision;
+    int32_t normuon;
+    float normuon_beta2;
+    float normuon_eps;
+    float weight_decay;
+} muon_hparams;
+
+/* Opaque handle: the host-side plan for one table on one device. */
+typedef struct muon_handle muon_handle;
+
+/* Fill *hp with the defaults above. */
+void muon_hparams_default(muon_hparams* hp);
+
+/* Bytes of device workspace muon_init needs for this table and hp.
+ * Host-only; validates the table (same errors as muon_init). */
+muon_status muon_workspace_bytes(const muon_matrix* table, int32_t n, const muon_hparams* hp,
+                                 size_t* out_bytes);
+
+/* Validate the host table, build the plan (short-side frame per matrix:
+ * matrices with rows > cols run transposed, [P4] Muon source; same-shape
+ * matrices batched per launch, [P2] change 2), upload descriptors into
+ * `workspace` (device, caller-owned, >= muon_workspace_bytes, 256-B aligned,
+ * kept for the handle's lifetime) and zero the NorMuon state. `device` is
+ * the HIP device index; it must be current in every later call.
+ * n = 0 is allowed (every step is then a no-op). On error *out is NULL. */
+muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp,
+                      void* workspace, size_t ws_bytes, int32_t device);
+
+/* One Muon step ([P4] Muon source; [P2] change 2), enqueued on `stream`:
+ * momentum + Nesterov, Frobenius normalisation, hp.ns_steps Newton–Schulz
+ * iterations, optional NorMuon, and
+ *   p <- p (1 - lr lr_mul wd wd_mul) - lr lr_mul max(1, rows/cols)^0.5 O.
+ * params, momentum: float32 device buffers of `numel` elements, updated in
+ * place; grads: float32 device buffer of `numel` elements, read only. All
+ * three share the table's layout and must not alias each other.
+ * momentum_coef < 0 uses hp.momentum (a per-call value supports momentum
+ * warm-up, [P3]); lr is the per-call learning rate (schedules live with the
+ * caller). Errors: MUON_E_LAYOUT if numel < the table's extent,
+ * MUON_E_INVALID_ARG for null buffers or non-finite lr. */
+muon_status muon_step(muon_handle* h, float* params, const float* grads, float* momentum, int64_t numel,
+                      float lr, float momentum_coef, void* stream);
+
+/* Zero the momentum of every non-frozen matrix in `momentum` (numel
+ * elements, may be NULL to skip) and the NorMuon second moment, on
+ * `stream` ([P2] change 2: reset() after warm-up / capture dirtied them). */
+muon_status muon_reset(muon_handle* h, float* momentum, int64_t numel, void* stream);
+
+/* Free the handle (host memory only). NULL is a no-op. */
+void muon_destroy(muon_handle* h);
+
+/* Static description of a status code. */
+const char* muon_status_string(muon_status s);
+
+/* Detail of the handle's last error ("" if none); NULL handle -> the last
+ * error of a failed muon_init / muon_workspace_bytes on this thread. */
+const char* muon_last_error(const muon_handle* h);
+
+/* ---- introspection (tests and tools) ------------------------------------ */
+
+/* Where matrix `index` (0-based over the table with counts expanded) lives
+ * in the workspace: short-side shape m <= n, row stride ld (elements) of the
+ * padded canonical buffers, element offsets into the X buffers and into the
+ * per-row NorMuon arrays, transposed = stored rows > cols, active = !frozen. */
+typedef struct muon_layout {
+    int64_t x_offset;
+    int64_t row_offset;
+    int32_t m, n, ld, m_pad;
+    int32_t transposed;
+    int32_t active;
+    int32_t stored_rows, stored_cols;
+    int64_t param_offset;
+} muon_layout;
+
+muon_status muon_matrix_layout(const muon_handle* h, int32_t index, muon_layout* out);
+
+/* Number of matrices (counts expanded). */
+int32_t muon_num_matrices(const muon_handle* h);
+
+enum {
+    MUON_VIEW_XTILDE = 0,  /* momentum kernel output: canonical, padded X~ (bf16 or fp32) */
+    MUON_VIEW_NS_OUT = 1,  /* final Newton–Schulz output, same layout */
+    MUON_VIEW_SUMSQ = 2,   /* float32 [num_matrices]: sum of u^2 */
+    MUON_VIEW_SCALE = 3,   /* float32 [num_matrices]: s = 1/(sqrt(sumsq) + ns_eps) */
+    MUON_VIEW_V = 4,       /* float32 per canonical row: NorMuon second moment */
+    MUON_VIEW_F = 5,       /* float32 per canonical row: NorMuon row factor */
+    MUON_VIEW_STATUS = 6   /* int32 [num_matrices]: bit 0 = non-finite u seen this step */
+};
+
+/* Device pointer and byte size of an internal buffer, valid after the
+ * stream work of the last muon_step has completed. */
+muon_status muon_debug_view(const muon_handle* h, int32_t which, void** dev_ptr, size_t* bytes);
+
+/* ---- measurement (benchmarks) ------------------------------------------- */
+
+enum {
+    MUON_KERNEL_MOMENTUM = 0, /* momentum + Nesterov + cast + sum of squares */
+    MUON_KERNEL_GRAM = 1,     /* A = X X^T (upper tiles, mirrored) */
+    MUON_KERNEL_POLY = 2,     /* B = b A + c A^2 */
+    MUON_KERNEL_UPDATE = 3,   /* X <- a X + B X */
+    MUON_KERNEL_NORMUON = 4,  /* NorMuon row factors */
+    MUON_KERNEL_APPLY = 5,    /* parameter update */
+    MUON_KERNEL_COUNT = 6
+};
+
+/* Algorithmic work of one muon_step for this plan (frozen matrices excluded).
+ * flops[k]: floating-point operations of kernel class k per step, counting a
+ * symmetric product (Gram, A^2) as m(m+1)k; bytes[k]: bytes a kernel class
+ * must move per step (momentum: g, m read, m, X~ written; apply: O, p read,
+ * p written; NorMuon: row partials, v, f); launches[k]: launches per step. */
+typedef struct muon_work {
+    double flops[MUON_KERNEL_COUNT];
+    double bytes[MUON_KERNEL_COUNT];
+    int64_t launches[MUON_KERNEL_COUNT];
+    int64_t active_elements;
+} muon_work;
+
+muon_status muon_work_stats(const muon_handle* h, muon_work* out);
+
+/* on != 0: every later muon_step records a pair of HIP events around each
+ * kernel launch on its stream (host-side records only, no device memory).
+ * on == 0 stops recording; recorded pairs are kept until read. */
+muon_status muon_profile_enable(muon_handle* h, int32_t on);
+
+/* Wait for the recorded events and return, for kernel class `kernel`, the
+ * number of recorded launches and their summed duration in milliseconds.
+ * clear != 0 drops every record afterwards. */
+muon_status muon_profile_read(muon_handle* h, int32_t kernel, int32_t clear, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMUON_H */

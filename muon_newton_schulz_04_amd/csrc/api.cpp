@@ -1,0 +1,458 @@
+// C ABI of libmuon (include/libmuon.h): handle lifecycle, argument checks,
+// and the launch sequence of one Muon step on the caller's stream.
+//
+// Step order ([P4] "modded-nanogpt 50B-token 长时程训练实验解析" section
+// "从源码看 Muon 的分布式正交化实现"; [P2] "2025-10-27_FixMuonLR" change 2):
+//   momentum + Nesterov -> X~ (short-side frame) and sum u^2
+//   ns_steps x (Gram, polynomial, update), normalisation folded into step 0
+//   NorMuon row factors (optional)
+//   parameter update
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/libmuon.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+struct muon_handle {
+    muon::Plan plan;
+    int device = 0;
+    char* ws = nullptr;
+    size_t ws_bytes = 0;
+    std::string last_error;
+    // optional per-launch event timing
+    struct Rec {
+        int kind;
+        hipEvent_t start, stop;
+    };
+    bool profiling = false;
+    std::vector<Rec> recs;          // recorded, not yet read
+    std::vector<hipEvent_t> spare;  // events for reuse
+    ~muon_handle() {
+        for (auto& r : recs) {
+            (void)hipEventDestroy(r.start);
+            (void)hipEventDestroy(r.stop);
+        }
+        for (auto e : spare) (void)hipEventDestroy(e);
+    }
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+muon_status fail(muon_handle* h, muon_status s, const std::string& msg) {
+    if (h)
+        h->last_error = msg;
+    else
+        g_last_error = msg;
+    return s;
+}
+
+muon_status hip_fail(muon_handle* h, hipError_t e, const char* where) {
+    std::string msg = std::string(where) + ": " + hipGetErrorString(e);
+    return fail(h, MUON_E_HIP, msg);
+}
+
+muon::LaunchCtx make_ctx(const muon_handle* h, hipStream_t stream) {
+    const muon::Plan& P = h->plan;
+    char* ws = h->ws;
+    muon::LaunchCtx L;
+    L.stream = stream;
+    L.fp32 = P.hp.ns_precision == MUON_NS_FP32;
+    L.mats = reinterpret_cast<const muon::MatDesc*>(ws + P.off_mats);
+    L.ew_map = reinterpret_cast<const int32_t*>(ws + P.off_ewmap);
+    L.active = reinterpret_cast<const int32_t*>(ws + P.off_active);
+    L.ew_tiles = (int)P.ew_map.size();
+    L.n_active = (int)P.active.size();
+    L.xt = ws + P.off_xt;
+    L.x0 = ws + P.off_x0;
+    L.x1 = ws + P.off_x1;
+    L.a = ws + P.off_a;
+    L.b = ws + P.off_b;
+    L.partials = reinterpret_cast<float*>(ws + P.off_part);
+    L.ss = reinterpret_cast<float*>(ws + P.off_ss);
+    L.scale = reinterpret_cast<float*>(ws + P.off_scale);
+    L.status = reinterpret_cast<int32_t*>(ws + P.off_status);
+    L.v = reinterpret_cast<float*>(ws + P.off_v);
+    L.f = reinterpret_cast<float*>(ws + P.off_f);
+    L.rowpart = reinterpret_cast<float*>(ws + P.off_rowpart);
+    L.rows_total = P.rows_total;
+    return L;
+}
+
+muon::GemmList make_list(const muon_handle* h, const muon::TileList& T) {
+    muon::GemmList G;
+    G.T = T.T;
+    G.gram = reinterpret_cast<const muon::TileWork*>(h->ws + T.off_gram);
+    G.n_gram = (int)T.gram.size();
+    G.poly = reinterpret_cast<const muon::TileWork*>(h->ws + T.off_poly);
+    G.n_poly = (int)T.poly.size();
+    G.update = reinterpret_cast<const muon::TileWork*>(h->ws + T.off_update);
+    G.n_update = (int)T.update.size();
+    return G;
+}
+
+// Final Newton–Schulz output buffer: iteration 0 writes x1, then x0 / x1 alternate.
+void* ns_out(const muon_handle* h) {
+    const muon::Plan& P = h->plan;
+    return h->ws + ((P.hp.ns_steps & 1) ? P.off_x1 : P.off_x0);
+}
+
+muon_status check_device(muon_handle* h) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(h, e, "hipGetDevice");
+    if (cur != h->device)
+        return fail(h, MUON_E_STATE, "device " + std::to_string(h->device) + " is not current (current is " +
+                                         std::to_string(cur) + ")");
+    return MUON_OK;
+}
+
+hipError_t take_event(muon_handle* h, hipEvent_t* ev) {
+    if (!h->spare.empty()) {
+        *ev = h->spare.back();
+        h->spare.pop_back();
+        return hipSuccess;
+    }
+    return hipEventCreate(ev);
+}
+
+bool overlap(const void* a, const void* b, int64_t bytes) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + bytes && y < x + bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status muon_workspace_bytes(const muon_matrix* table, int32_t n, const muon_hparams* hp, size_t* out_bytes) {
+    if (!out_bytes) return fail(nullptr, MUON_E_INVALID_ARG, "null out_bytes");
+    muon::Plan P;
+    std::string err;
+    muon_status s = muon::build_plan(table, n, hp, &P, &err);
+    if (s != MUON_OK) return fail(nullptr, s, err);
+    *out_bytes = P.total_bytes;
+    return MUON_OK;
+}
+
+muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp, void* workspace,
+                      size_t ws_bytes, int32_t device) {
+    if (!out) return fail(nullptr, MUON_E_INVALID_ARG, "null handle output");
+    *out = nullptr;
+    muon_handle* h = new muon_handle();
+    std::string err;
+    muon_status s = muon::build_plan(table, n, hp, &h->plan, &err);
+    if (s != MUON_OK) {
+        delete h;
+        return fail(nullptr, s, err);
+    }
+    const muon::Plan& P = h->plan;
+    if (P.total_bytes > 0) {
+        if (!workspace) {
+            delete h;
+            return fail(nullptr, MUON_E_WORKSPACE, "null workspace");
+        }
+        if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) {
+            delete h;
+            return fail(nullptr, MUON_E_WORKSPACE, "workspace not 256-byte aligned");
+        }
+        if (ws_bytes < P.total_bytes) {
+            delete h;
+            return fail(nullptr, MUON_E_WORKSPACE,
+                        "workspace too small: need " + std::to_string(P.total_bytes) + " bytes");
+        }
+    }
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count < 1) {
+        delete h;
+        return fail(nullptr, MUON_E_NO_DEVICE, "no HIP device");
+    }
+    if (device < 0 || device >= count) {
+        delete h;
+        return fail(nullptr, MUON_E_NO_DEVICE, "device index out of range");
+    }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(nullptr, e, "hipGetDeviceProperties");
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+        delete h;
+        return fail(nullptr, MUON_E_NO_DEVICE, std::string("device is ") + prop.gcnArchName + ", need gfx950");
+    }
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    e = hipSetDevice(device);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(nullptr, e, "hipSetDevice");
+    }
+    h->device = device;
+    h->ws = static_cast<char*>(workspace);
+    h->ws_bytes = ws_bytes;
+    auto up = [&](size_t off, const void* src, size_t bytes) -> hipError_t {
+        if (bytes == 0) return hipSuccess;
+        return hipMemcpy(h->ws + off, src, bytes, hipMemcpyHostToDevice);
+    };
+    e = up(P.off_mats, P.mats.data(), P.mats.size() * sizeof(muon::MatDesc));
+    if (e == hipSuccess) e = up(P.off_ewmap, P.ew_map.data(), P.ew_map.size() * 4);
+    if (e == hipSuccess) e = up(P.off_active, P.active.data(), P.active.size() * 4);
+    for (const auto& L : P.lists) {
+        if (e == hipSuccess) e = up(L.off_gram, L.gram.data(), L.gram.size() * sizeof(muon::TileWork));
+        if (e == hipSuccess) e = up(L.off_poly, L.poly.data(), L.poly.size() * sizeof(muon::TileWork));
+        if (e == hipSuccess) e = up(L.off_update, L.update.data(), L.update.size() * sizeof(muon::TileWork));
+    }
+    if (e == hipSuccess && P.rows_total) e = hipMemset(h->ws + P.off_v, 0, (size_t)P.rows_total * 4);
+    if (e == hipSuccess && P.mats.size()) e = hipMemset(h->ws + P.off_status, 0, P.mats.size() * 4);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (prev >= 0) (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(nullptr, e, "uploading descriptors");
+    }
+    *out = h;
+    return MUON_OK;
+}
+
+muon_status muon_step(muon_handle* h, float* params, const float* grads, float* momentum, int64_t numel, float lr,
+                      float momentum_coef, void* stream) {
+    if (!h) return fail(nullptr, MUON_E_INVALID_ARG, "null handle");
+    const muon::Plan& P = h->plan;
+    if (P.active.empty()) return MUON_OK;
+    if (!params || !grads || !momentum) return fail(h, MUON_E_INVALID_ARG, "null params / grads / momentum");
+    if (numel < P.extent)
+        return fail(h, MUON_E_LAYOUT, "buffers hold " + std::to_string(numel) + " elements, table needs " +
+                                          std::to_string(P.extent));
+    if ((reinterpret_cast<uintptr_t>(params) | reinterpret_cast<uintptr_t>(grads) |
+         reinterpret_cast<uintptr_t>(momentum)) % 16 != 0)
+        return fail(h, MUON_E_LAYOUT, "params / grads / momentum must be 16-byte aligned");
+    const int64_t bytes = numel * 4;
+    if (overlap(params, grads, bytes) || overlap(params, momentum, bytes) || overlap(grads, momentum, bytes))
+        return fail(h, MUON_E_INVALID_ARG, "params, grads and momentum must not overlap");
+    if (!std::isfinite(lr)) return fail(h, MUON_E_INVALID_ARG, "non-finite lr");
+    float beta = P.hp.momentum;
+    if (momentum_coef >= 0.f) {
+        if (!(momentum_coef <= 1.f)) return fail(h, MUON_E_INVALID_ARG, "momentum_coef must be in [0, 1]");
+        beta = momentum_coef;
+    } else if (!(momentum_coef < 0.f)) {
+        return fail(h, MUON_E_INVALID_ARG, "momentum_coef is NaN");
+    }
+    muon_status s = check_device(h);
+    if (s != MUON_OK) return s;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const muon::LaunchCtx L = make_ctx(h, st);
+    hipError_t e = hipSuccess;
+    // run one launch, bracketed by events when profiling
+    auto run = [&](int kind, const char* what, auto&& launch) -> muon_status {
+        hipEvent_t a = nullptr, b = nullptr;
+        if (h->profiling) {
+            hipError_t pe = take_event(h, &a);
+            if (pe == hipSuccess) pe = take_event(h, &b);
+            if (pe == hipSuccess) pe = hipEventRecord(a, st);
+            if (pe != hipSuccess) return hip_fail(h, pe, "profiling event");
+        }
+        hipError_t le = launch();
+        if (le != hipSuccess) return hip_fail(h, le, what);
+        if (h->profiling) {
+            hipError_t pe = hipEventRecord(b, st);
+            if (pe != hipSuccess) return hip_fail(h, pe, "profiling event");
+            h->recs.push_back({kind, a, b});
+        }
+        return MUON_OK;
+    };
+    s = run(MUON_KERNEL_MOMENTUM, "momentum kernel", [&] {
+        return muon::launch_momentum(L, grads, momentum, beta, P.hp.nesterov,
+                                     P.hp.momentum_kind == MUON_MOMENTUM_HEAVY_BALL);
+    });
+    if (s != MUON_OK) return s;
+
+    const int steps = P.hp.ns_steps;
+    for (int k = 0; k < steps; ++k) {
+        void* xin = k == 0 ? L.xt : ((k & 1) ? L.x1 : L.x0);
+        void* xout = k == 0 ? L.x1 : ((k & 1) ? L.x0 : L.x1);
+        const float ca = P.hp.ns_coeffs[k][0], cb = P.hp.ns_coeffs[k][1], cc = P.hp.ns_coeffs[k][2];
+        const int first = k == 0;
+        const int rowstats = (k == steps - 1) && P.hp.normuon;
+        for (const auto& T : P.lists) {
+            const muon::GemmList G = make_list(h, T);
+            s = run(MUON_KERNEL_GRAM, "Gram kernel", [&] {
+                return muon::launch_ns_stage(L, G, muon::NS_GRAM, xin, nullptr, L.a, ca, cb, cc, first,
+                                             P.hp.ns_eps, 0);
+            });
+            if (s != MUON_OK) return s;
+            s = run(MUON_KERNEL_POLY, "polynomial kernel", [&] {
+                return muon::launch_ns_stage(L, G, muon::NS_POLY, nullptr, L.a, L.b, ca, cb, cc, first,
+                                             P.hp.ns_eps, 0);
+            });
+            if (s != MUON_OK) return s;
+            s = run(MUON_KERNEL_UPDATE, "update kernel", [&] {
+                return muon::launch_ns_stage(L, G, muon::NS_UPDATE, xin, L.b, xout, ca, cb, cc, first,
+                                             P.hp.ns_eps, rowstats);
+            });
+            if (s != MUON_OK) return s;
+        }
+    }
+    const float* f = nullptr;
+    if (P.hp.normuon) {
+        s = run(MUON_KERNEL_NORMUON, "NorMuon kernel",
+                [&] { return muon::launch_normuon(L, P.hp.normuon_beta2, P.hp.normuon_eps); });
+        if (s != MUON_OK) return s;
+        f = L.f;
+    }
+    s = run(MUON_KERNEL_APPLY, "apply kernel",
+            [&] { return muon::launch_apply(L, ns_out(h), f, params, lr, P.hp.weight_decay); });
+    (void)e;
+    return s;
+}
+
+muon_status muon_reset(muon_handle* h, float* momentum, int64_t numel, void* stream) {
+    if (!h) return fail(nullptr, MUON_E_INVALID_ARG, "null handle");
+    const muon::Plan& P = h->plan;
+    if (P.active.empty()) return MUON_OK;
+    if (momentum) {
+        if (numel < P.extent) return fail(h, MUON_E_LAYOUT, "momentum buffer smaller than the table extent");
+    }
+    muon_status s = check_device(h);
+    if (s != MUON_OK) return s;
+    const muon::LaunchCtx L = make_ctx(h, static_cast<hipStream_t>(stream));
+    hipError_t e = muon::launch_reset(L, momentum);
+    if (e != hipSuccess) return hip_fail(h, e, "reset kernels");
+    return MUON_OK;
+}
+
+void muon_destroy(muon_handle* h) { delete h; }
+
+const char* muon_status_string(muon_status s) {
+    switch (s) {
+        case MUON_OK: return "ok";
+        case MUON_E_INVALID_ARG: return "invalid argument";
+        case MUON_E_SHAPE: return "invalid matrix shape";
+        case MUON_E_LAYOUT: return "invalid buffer layout";
+        case MUON_E_NO_DEVICE: return "no usable gfx950 device";
+        case MUON_E_HIP: return "HIP runtime error";
+        case MUON_E_STATE: return "invalid handle state";
+        case MUON_E_WORKSPACE: return "invalid workspace";
+    }
+    return "unknown status";
+}
+
+const char* muon_last_error(const muon_handle* h) {
+    if (!h) return g_last_error.c_str();
+    return h->last_error.c_str();
+}
+
+int32_t muon_num_matrices(const muon_handle* h) { return h ? (int32_t)h->plan.mats.size() : 0; }
+
+muon_status muon_matrix_layout(const muon_handle* h, int32_t index, muon_layout* out) {
+    if (!h || !out) return MUON_E_INVALID_ARG;
+    if (index < 0 || index >= (int32_t)h->plan.mats.size()) return MUON_E_INVALID_ARG;
+    const muon::MatDesc& d = h->plan.mats[index];
+    out->x_offset = d.x_off;
+    out->row_offset = d.row_off;
+    out->m = d.m;
+    out->n = d.n;
+    out->ld = d.n_pad;
+    out->m_pad = d.m_pad;
+    out->transposed = d.transposed;
+    out->active = h->plan.active_flag[index];
+    out->stored_rows = d.R;
+    out->stored_cols = d.C;
+    out->param_offset = d.p_off;
+    return MUON_OK;
+}
+
+muon_status muon_debug_view(const muon_handle* h, int32_t which, void** dev_ptr, size_t* bytes) {
+    if (!h || !dev_ptr || !bytes) return MUON_E_INVALID_ARG;
+    const muon::Plan& P = h->plan;
+    const size_t nm = P.mats.size();
+    switch (which) {
+        case MUON_VIEW_XTILDE: *dev_ptr = h->ws + P.off_xt; *bytes = (size_t)P.x_elems * P.esize; break;
+        case MUON_VIEW_NS_OUT: *dev_ptr = ns_out(h); *bytes = (size_t)P.x_elems * P.esize; break;
+        case MUON_VIEW_SUMSQ: *dev_ptr = h->ws + P.off_ss; *bytes = nm * 4; break;
+        case MUON_VIEW_SCALE: *dev_ptr = h->ws + P.off_scale; *bytes = nm * 4; break;
+        case MUON_VIEW_V: *dev_ptr = h->ws + P.off_v; *bytes = (size_t)P.rows_total * 4; break;
+        case MUON_VIEW_F: *dev_ptr = h->ws + P.off_f; *bytes = (size_t)P.rows_total * 4; break;
+        case MUON_VIEW_STATUS: *dev_ptr = h->ws + P.off_status; *bytes = nm * 4; break;
+        default: return MUON_E_INVALID_ARG;
+    }
+    return MUON_OK;
+}
+
+muon_status muon_work_stats(const muon_handle* h, muon_work* out) {
+    if (!h || !out) return MUON_E_INVALID_ARG;
+    std::memset(out, 0, sizeof(*out));
+    const muon::Plan& P = h->plan;
+    const int steps = P.hp.ns_steps;
+    const double es = P.esize;
+    int64_t act = 0;
+    double rows = 0, rowpart = 0;
+    for (int32_t mi : P.active) {
+        const muon::MatDesc& d = P.mats[mi];
+        const double m = d.m, n = d.n;
+        out->flops[MUON_KERNEL_GRAM] += steps * m * (m + 1) * n;
+        out->flops[MUON_KERNEL_POLY] += steps * m * (m + 1) * m;
+        out->flops[MUON_KERNEL_UPDATE] += steps * 2.0 * m * m * n;
+        act += (int64_t)d.m * d.n;
+        rows += m;
+        rowpart += (double)(d.n_pad / d.T) * m;
+    }
+    out->active_elements = act;
+    out->bytes[MUON_KERNEL_MOMENTUM] = (double)act * (12.0 + es);
+    out->bytes[MUON_KERNEL_APPLY] = (double)act * (8.0 + es);
+    if (P.hp.normuon) out->bytes[MUON_KERNEL_NORMUON] = 4.0 * (rowpart + 3.0 * rows);
+    const int64_t nl = (int64_t)P.lists.size();
+    const int64_t any = P.active.empty() ? 0 : 1;
+    out->launches[MUON_KERNEL_MOMENTUM] = any;
+    out->launches[MUON_KERNEL_GRAM] = steps * nl;
+    out->launches[MUON_KERNEL_POLY] = steps * nl;
+    out->launches[MUON_KERNEL_UPDATE] = steps * nl;
+    out->launches[MUON_KERNEL_NORMUON] = P.hp.normuon ? any : 0;
+    out->launches[MUON_KERNEL_APPLY] = any;
+    return MUON_OK;
+}
+
+muon_status muon_profile_enable(muon_handle* h, int32_t on) {
+    if (!h) return MUON_E_INVALID_ARG;
+    h->profiling = on != 0;
+    return MUON_OK;
+}
+
+muon_status muon_profile_read(muon_handle* h, int32_t kernel, int32_t clear, int64_t* launches, double* total_ms) {
+    if (!h || !launches || !total_ms) return MUON_E_INVALID_ARG;
+    if (kernel < 0 || kernel >= MUON_KERNEL_COUNT) return MUON_E_INVALID_ARG;
+    int64_t n = 0;
+    double tot = 0.0;
+    for (auto& r : h->recs) {
+        if (r.kind != kernel) continue;
+        hipError_t e = hipEventSynchronize(r.stop);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess) return hip_fail(h, e, "reading profiling events");
+        ++n;
+        tot += ms;
+    }
+    *launches = n;
+    *total_ms = tot;
+    if (clear) {
+        for (auto& r : h->recs) {
+            (void)hipEventSynchronize(r.stop);
+            h->spare.push_back(r.start);
+            h->spare.push_back(r.stop);
+        }
+        h->recs.clear();
+    }
+    return MUON_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,397 @@
+// HBM-streaming kernels of the Muon step: momentum (+ Nesterov, cast to the
+// Newton–Schulz input, per-matrix sum of squares), the NorMuon row factors,
+// the parameter update, and the reset fills.
+//
+// Sources: [P4] "modded-nanogpt 50B-token 长时程训练实验解析" section
+// "从源码看 Muon 的分布式正交化实现" (momentum + Nesterov, Frobenius normalisation,
+// transpose to the short side, max(1, rows/cols)^0.5, p -= lr * update);
+// [P2] "2025-10-27_FixMuonLR" analysis, change 2 (lerp momentum buffer,
+// NorMuon per-lane second moment along the longer dimension).
+//
+// All kernels work on 64 x 64 tiles of a matrix's padded canonical frame
+// (rows <= cols). Matrices stored with rows > cols are transposed through
+// LDS so that both the stored-frame and canonical-frame accesses stay
+// coalesced.
+
+#include "kernel_common.hpp"
+#include "launch.hpp"
+
+namespace muon {
+
+namespace {
+
+constexpr int TS = kEwTile;  // 64
+
+struct TileCoord {
+    int mi, i0, j0;
+};
+
+__device__ __forceinline__ TileCoord decode_tile(const MatDesc& d, int tile, int mi) {
+    const int lt = tile - d.ew_start;
+    const int ti = lt / d.ew_tiles_n;
+    const int tj = lt - ti * d.ew_tiles_n;
+    return {mi, ti * TS, tj * TS};
+}
+
+struct MomParams {
+    float beta;
+    int nesterov;
+    int heavy;
+};
+
+// m <- beta m + (1-beta) g  (lerp)   |  m <- beta m + g   (heavy ball)
+// u =  (1-beta) g + beta m_new       |  u =  g + beta m_new   (Nesterov)
+__device__ __forceinline__ float mom_update(float g, float& m, const MomParams& P) {
+    const float gs = P.heavy ? g : (1.0f - P.beta) * g;
+    const float mn = fmaf(P.beta, m, gs);
+    m = mn;
+    return P.nesterov ? fmaf(P.beta, mn, gs) : mn;
+}
+
+template <typename XT>
+__device__ __forceinline__ void store_x4(XT* dst, float a, float b, float c, float d);
+
+template <>
+__device__ __forceinline__ void store_x4<bf16>(bf16* dst, float a, float b, float c, float d) {
+    uint2 w;
+    w.x = pack_bf16x2(a, b);
+    w.y = pack_bf16x2(c, d);
+    *reinterpret_cast<uint2*>(dst) = w;
+}
+
+template <>
+__device__ __forceinline__ void store_x4<float>(float* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+
+template <typename XT>
+__device__ __forceinline__ void load_x4(const XT* src, float* v);
+
+template <>
+__device__ __forceinline__ void load_x4<bf16>(const bf16* src, float* v) {
+    const uint2 w = *reinterpret_cast<const uint2*>(src);
+    v[0] = bf16_lo(w.x);
+    v[1] = bf16_hi(w.x);
+    v[2] = bf16_lo(w.y);
+    v[3] = bf16_hi(w.y);
+}
+
+template <>
+__device__ __forceinline__ void load_x4<float>(const float* src, float* v) {
+    const float4 w = *reinterpret_cast<const float4*>(src);
+    v[0] = w.x;
+    v[1] = w.y;
+    v[2] = w.z;
+    v[3] = w.w;
+}
+
+// ---------------------------------------------------------------------------
+// K1: momentum + Nesterov + cast into the canonical Newton–Schulz input,
+// and one deterministic sum of u^2 per tile.
+// Thread layout in a 64 x 64 tile: 16 column groups of 4 x 16 row lanes,
+// four passes of 16 rows.
+// ---------------------------------------------------------------------------
+template <typename XT>
+__global__ __launch_bounds__(kThreads) void k_momentum(const MatDesc* __restrict__ mats,
+                                                       const int32_t* __restrict__ ew_map,
+                                                       const float* __restrict__ grads,
+                                                       float* __restrict__ mom, XT* __restrict__ xt,
+                                                       float* __restrict__ partials, MomParams P) {
+    __shared__ float lds[TS][TS + 1];
+    __shared__ float red[4];
+    const int tile = blockIdx.x;
+    const int mi = ew_map[tile];
+    const MatDesc d = mats[mi];
+    const TileCoord tc = decode_tile(d, tile, mi);
+    const int tid = threadIdx.x;
+    const int cg = (tid & 15) * 4;
+    const int rg = tid >> 4;
+    float ssq = 0.0f;
+
+    if (!d.transposed) {
+        // canonical (i, j) == stored (i, j)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int i = tc.i0 + rg + 16 * p;
+            const int j = tc.j0 + cg;
+            float u[4] = {0.f, 0.f, 0.f, 0.f};
+            if (i < d.m) {
+                const int64_t base = d.p_off + (int64_t)i * d.C + j;
+                if (d.vec_ok && j + 3 < d.n) {
+                    const float4 g4 = *reinterpret_cast<const float4*>(grads + base);
+                    float4 m4 = *reinterpret_cast<const float4*>(mom + base);
+                    u[0] = mom_update(g4.x, m4.x, P);
+                    u[1] = mom_update(g4.y, m4.y, P);
+                    u[2] = mom_update(g4.z, m4.z, P);
+                    u[3] = mom_update(g4.w, m4.w, P);
+                    *reinterpret_cast<float4*>(mom + base) = m4;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (j + e < d.n) {
+                            float mv = mom[base + e];
+                            u[e] = mom_update(grads[base + e], mv, P);
+                            mom[base + e] = mv;
+                        }
+                    }
+                }
+            }
+            ssq = fmaf(u[0], u[0], ssq);
+            ssq = fmaf(u[1], u[1], ssq);
+            ssq = fmaf(u[2], u[2], ssq);
+            ssq = fmaf(u[3], u[3], ssq);
+            store_x4<XT>(xt + d.x_off + (int64_t)i * d.n_pad + j, u[0], u[1], u[2], u[3]);
+        }
+    } else {
+        // canonical (i, j) == stored (j, i); stored rows r = j0.., cols c = i0..
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int rl = rg + 16 * p;
+            const int r = tc.j0 + rl;
+            const int c = tc.i0 + cg;
+            float u[4] = {0.f, 0.f, 0.f, 0.f};
+            if (r < d.R) {
+                const int64_t base = d.p_off + (int64_t)r * d.C + c;
+                if (d.vec_ok && c + 3 < d.C) {
+                    const float4 g4 = *reinterpret_cast<const float4*>(grads + base);
+                    float4 m4 = *reinterpret_cast<const float4*>(mom + base);
+                    u[0] = mom_update(g4.x, m4.x, P);
+                    u[1] = mom_update(g4.y, m4.y, P);
+                    u[2] = mom_update(g4.z, m4.z, P);
+                    u[3] = mom_update(g4.w, m4.w, P);
+                    *reinterpret_cast<float4*>(mom + base) = m4;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (c + e < d.C) {
+                            float mv = mom[base + e];
+                            u[e] = mom_update(grads[base + e], mv, P);
+                            mom[base + e] = mv;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ssq = fmaf(u[e], u[e], ssq);
+                lds[cg + e][rl] = u[e];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int il = rg + 16 * p;
+            const int i = tc.i0 + il;
+            const int j = tc.j0 + cg;
+            store_x4<XT>(xt + d.x_off + (int64_t)i * d.n_pad + j, lds[il][cg], lds[il][cg + 1],
+                         lds[il][cg + 2], lds[il][cg + 3]);
+        }
+    }
+    const float t = block_sum_256(ssq, red);
+    if (tid == 0) partials[tile] = t;
+}
+
+// ---------------------------------------------------------------------------
+// K6: p <- p (1 - lr lr_mul wd wd_mul) - lr lr_mul shape_scale f_row O
+// (f_row = NorMuon factor of the canonical row, 1 without NorMuon).
+// ---------------------------------------------------------------------------
+template <typename XT>
+__global__ __launch_bounds__(kThreads) void k_apply(const MatDesc* __restrict__ mats,
+                                                    const int32_t* __restrict__ ew_map,
+                                                    const XT* __restrict__ xo, const float* __restrict__ fr,
+                                                    float* __restrict__ params, float lr, float wd) {
+    __shared__ float lds[TS][TS + 1];
+    const int tile = blockIdx.x;
+    const int mi = ew_map[tile];
+    const MatDesc d = mats[mi];
+    const TileCoord tc = decode_tile(d, tile, mi);
+    if (tc.i0 >= d.m || tc.j0 >= d.n) return;  // tile lies wholly in the padding
+    const int tid = threadIdx.x;
+    const int cg = (tid & 15) * 4;
+    const int rg = tid >> 4;
+    const float lrm = lr * d.lr_mul;
+    const float decay = 1.0f - lrm * wd * d.wd_mul;
+    const float coef0 = lrm * d.shape_scale;
+
+    if (!d.transposed) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int i = tc.i0 + rg + 16 * p;
+            const int j = tc.j0 + cg;
+            if (i >= d.m) continue;
+            float x[4];
+            load_x4<XT>(xo + d.x_off + (int64_t)i * d.n_pad + j, x);
+            const float coef = fr ? coef0 * fr[d.row_off + i] : coef0;
+            const int64_t base = d.p_off + (int64_t)i * d.C + j;
+            if (d.vec_ok && j + 3 < d.n) {
+                float4 p4 = *reinterpret_cast<float4*>(params + base);
+                p4.x = fmaf(-coef, x[0], p4.x * decay);
+                p4.y = fmaf(-coef, x[1], p4.y * decay);
+                p4.z = fmaf(-coef, x[2], p4.z * decay);
+                p4.w = fmaf(-coef, x[3], p4.w * decay);
+                *reinterpret_cast<float4*>(params + base) = p4;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < d.n) params[base + e] = fmaf(-coef, x[e], params[base + e] * decay);
+            }
+        }
+    } else {
+        // read canonical rows (i = stored column), write stored rows
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int il = rg + 16 * p;
+            const int i = tc.i0 + il;
+            const int j = tc.j0 + cg;
+            float x[4];
+            load_x4<XT>(xo + d.x_off + (int64_t)i * d.n_pad + j, x);
+            lds[cg][il] = x[0];
+            lds[cg + 1][il] = x[1];
+            lds[cg + 2][il] = x[2];
+            lds[cg + 3][il] = x[3];
+        }
+        __syncthreads();
+        float coef[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = tc.i0 + cg + e;
+            coef[e] = (fr && c < d.C) ? coef0 * fr[d.row_off + c] : coef0;
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int rl = rg + 16 * p;
+            const int r = tc.j0 + rl;
+            const int c = tc.i0 + cg;
+            if (r >= d.R) continue;
+            const int64_t base = d.p_off + (int64_t)r * d.C + c;
+            if (d.vec_ok && c + 3 < d.C) {
+                float4 p4 = *reinterpret_cast<float4*>(params + base);
+                p4.x = fmaf(-coef[0], lds[rl][cg], p4.x * decay);
+                p4.y = fmaf(-coef[1], lds[rl][cg + 1], p4.y * decay);
+                p4.z = fmaf(-coef[2], lds[rl][cg + 2], p4.z * decay);
+                p4.w = fmaf(-coef[3], lds[rl][cg + 3], p4.w * decay);
+                *reinterpret_cast<float4*>(params + base) = p4;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c + e < d.C) params[base + e] = fmaf(-coef[e], lds[rl][cg + e], params[base + e] * decay);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K5: NorMuon factors, one block per active matrix.
+//   r_i = (1/n) sum_j O_ij^2   (row partials written by the last NS update)
+//   v_i <- beta2 v_i + (1 - beta2) r_i
+//   d_i = sqrt(v_i) + eps
+//   f_i = gamma / d_i, gamma = sqrt(sum_i r_i / sum_i r_i / d_i^2)  (keeps ||O||_F)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_normuon(const MatDesc* __restrict__ mats,
+                                                      const int32_t* __restrict__ active,
+                                                      const float* __restrict__ rowpart,
+                                                      float* __restrict__ v, float* __restrict__ f,
+                                                      float beta2, float eps) {
+    __shared__ float red[4];
+    const int mi = active[blockIdx.x];
+    const MatDesc d = mats[mi];
+    const int ntn = d.n_pad / d.T;
+    const float inv_n = 1.0f / (float)d.n;
+    float s1 = 0.f, s2 = 0.f;
+    for (int i = threadIdx.x; i < d.m; i += kThreads) {
+        float r = 0.f;
+        for (int t = 0; t < ntn; ++t) r += rowpart[d.rowpart_off + (int64_t)t * d.m_pad + i];
+        r *= inv_n;
+        const float vi = fmaf(beta2, v[d.row_off + i], (1.0f - beta2) * r);
+        v[d.row_off + i] = vi;
+        const float di = sqrtf(vi) + eps;
+        s1 += r;
+        s2 += r / (di * di);
+        f[d.row_off + i] = di;
+    }
+    const float S1 = block_sum_256(s1, red);
+    __syncthreads();
+    const float S2 = block_sum_256(s2, red);
+    const float gamma = S2 > 0.f ? sqrtf(S1 / S2) : 0.f;
+    for (int i = threadIdx.x; i < d.m; i += kThreads) f[d.row_off + i] = gamma / f[d.row_off + i];
+}
+
+// ---------------------------------------------------------------------------
+// Reset fills: zero the momentum of active matrices (stored extent, tile by
+// tile) and a float range.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_zero_momentum(const MatDesc* __restrict__ mats,
+                                                            const int32_t* __restrict__ ew_map,
+                                                            float* __restrict__ mom) {
+    const int tile = blockIdx.x;
+    const int mi = ew_map[tile];
+    const MatDesc d = mats[mi];
+    const TileCoord tc = decode_tile(d, tile, mi);
+    if (tc.i0 >= d.m || tc.j0 >= d.n) return;
+    const int tid = threadIdx.x;
+    const int cg = (tid & 15) * 4;
+    const int rg = tid >> 4;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int il = tc.i0 + rg + 16 * p;
+        const int jl = tc.j0 + cg;
+        // element (il, jl + e) of the canonical frame lives at stored (il, jl + e)
+        // or (jl + e, il); zero whichever is valid
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = il, j = jl + e;
+            if (i < d.m && j < d.n) {
+                const int64_t idx = d.transposed ? d.p_off + (int64_t)j * d.C + i : d.p_off + (int64_t)i * d.C + j;
+                mom[idx] = 0.f;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_fill_zero(float* __restrict__ x, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) x[i] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_momentum(const LaunchCtx& L, const float* grads, float* mom, float beta, int nesterov,
+                           int heavy) {
+    if (L.ew_tiles == 0) return hipSuccess;
+    MomParams P{beta, nesterov, heavy};
+    if (L.fp32)
+        k_momentum<float><<<L.ew_tiles, kThreads, 0, L.stream>>>(L.mats, L.ew_map, grads, mom,
+                                                                 (float*)L.xt, L.partials, P);
+    else
+        k_momentum<bf16><<<L.ew_tiles, kThreads, 0, L.stream>>>(L.mats, L.ew_map, grads, mom, (bf16*)L.xt,
+                                                                L.partials, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply(const LaunchCtx& L, const void* xo, const float* f, float* params, float lr, float wd) {
+    if (L.ew_tiles == 0) return hipSuccess;
+    if (L.fp32)
+        k_apply<float><<<L.ew_tiles, kThreads, 0, L.stream>>>(L.mats, L.ew_map, (const float*)xo, f, params, lr,
+                                                              wd);
+    else
+        k_apply<bf16><<<L.ew_tiles, kThreads, 0, L.stream>>>(L.mats, L.ew_map, (const bf16*)xo, f, params, lr, wd);
+    return hipGetLastError();
+}
+
+hipError_t launch_normuon(const LaunchCtx& L, float beta2, float eps) {
+    if (L.n_active == 0) return hipSuccess;
+    k_normuon<<<L.n_active, kThreads, 0, L.stream>>>(L.mats, L.active, L.rowpart, L.v, L.f, beta2, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_reset(const LaunchCtx& L, float* mom) {
+    if (mom && L.ew_tiles) k_zero_momentum<<<L.ew_tiles, kThreads, 0, L.stream>>>(L.mats, L.ew_map, mom);
+    if (L.rows_total) {
+        const int64_t n = L.rows_total;
+        const int blocks = (int)((n + kThreads - 1) / kThreads < 1024 ? (n + kThreads - 1) / kThreads : 1024);
+        k_fill_zero<<<blocks, kThreads, 0, L.stream>>>(L.v, n);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,63 @@
+// Host-side launchers of the libmuon kernels (internal interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_types.hpp"
+
+namespace muon {
+
+// Device addresses inside the caller's workspace plus launch geometry.
+struct LaunchCtx {
+    hipStream_t stream;
+    int fp32;                 // Newton–Schulz precision: 0 bf16, 1 fp32
+    const MatDesc* mats;
+    const int32_t* ew_map;    // elementwise tile -> matrix
+    const int32_t* active;    // active matrix indices
+    int ew_tiles;
+    int n_active;
+    void* xt;                 // momentum output X~ (canonical, padded)
+    void* x0;                 // ping-pong X buffers
+    void* x1;
+    void* a;                  // Gram A
+    void* b;                  // polynomial B
+    float* partials;          // per elementwise tile sum of u^2
+    float* ss;                // per matrix sum of u^2
+    float* scale;             // per matrix s
+    int32_t* status;          // per matrix flags
+    float* v;                 // NorMuon second moment (per canonical row)
+    float* f;                 // NorMuon row factor
+    float* rowpart;           // NorMuon row partial sums
+    int64_t rows_total;
+};
+
+// One grouped GEMM launch: a work list of output tiles, all with tile size T.
+struct GemmList {
+    int T;
+    const TileWork* gram;
+    int n_gram;
+    const TileWork* poly;
+    int n_poly;
+    const TileWork* update;
+    int n_update;
+};
+
+enum NsMode { NS_GRAM = 0, NS_POLY = 1, NS_UPDATE = 2 };
+
+hipError_t launch_momentum(const LaunchCtx& L, const float* grads, float* mom, float beta, int nesterov,
+                           int heavy);
+hipError_t launch_apply(const LaunchCtx& L, const void* xo, const float* f, float* params, float lr, float wd);
+hipError_t launch_normuon(const LaunchCtx& L, float beta2, float eps);
+hipError_t launch_reset(const LaunchCtx& L, float* mom);
+
+// One Newton–Schulz iteration stage over a work list.
+//   GRAM:   out = alpha * X X^T (upper tiles, mirrored); iteration 0: alpha = s^2
+//           from the momentum partials (and s, sum u^2, status are recorded)
+//   POLY:   out = b A + c A A^T (upper tiles, mirrored)
+//   UPDATE: out = a alpha X + alpha B X; iteration 0: alpha = s, else 1;
+//           rowstats: per-row partial sums of out^2 for NorMuon
+hipError_t launch_ns_stage(const LaunchCtx& L, const GemmList& G, int mode, const void* xin, const void* ain,
+                           void* out, float ca, float cb, float cc, int first, float eps, int rowstats);
+
+}  // namespace muon

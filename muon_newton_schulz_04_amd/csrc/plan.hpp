@@ -1,0 +1,55 @@
+// Host planner of libmuon: validates the matrix table, puts every matrix in
+// its short-side frame, groups matrices by GEMM tile size, orders the tile
+// work lists for the 8 XCDs, and lays out the workspace. Pure C++ (no HIP).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/libmuon.h"
+#include "device_types.hpp"
+
+namespace muon {
+
+struct TileList {
+    int T = 0;
+    std::vector<TileWork> gram, poly, update;
+    size_t off_gram = 0, off_poly = 0, off_update = 0;  // workspace byte offsets
+};
+
+struct Plan {
+    muon_hparams hp{};
+    int esize = 2;                      // bytes per Newton–Schulz element (bf16 / fp32)
+    std::vector<MatDesc> mats;          // every matrix, counts expanded
+    std::vector<uint8_t> active_flag;   // !frozen
+    std::vector<int32_t> active;        // active matrix indices
+    std::vector<int32_t> ew_map;        // elementwise tile -> matrix
+    std::vector<TileList> lists;        // one per tile size in use
+    int64_t extent = 0;                 // elements the flat buffers must hold
+    int64_t x_elems = 0, a_elems = 0, rows_total = 0, rowpart_elems = 0;
+    // workspace byte offsets
+    size_t off_xt = 0, off_x0 = 0, off_x1 = 0, off_a = 0, off_b = 0;
+    size_t off_part = 0, off_ss = 0, off_scale = 0, off_status = 0;
+    size_t off_v = 0, off_f = 0, off_rowpart = 0;
+    size_t off_mats = 0, off_ewmap = 0, off_active = 0;
+    size_t total_bytes = 0;
+    // 64-bit sums used by tools and tests
+    double ns_alg_flops = 0.0;          // per step, symmetric products counted as m(m+1)k
+};
+
+// Validate and build. Returns MUON_OK or an error code with *err set.
+muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* hp, Plan* out, std::string* err);
+
+// Validate hyper-parameters only.
+muon_status check_hparams(const muon_hparams* hp, std::string* err);
+
+// Order one list of tiles for the XCD round-robin dispatch: matrices are
+// assigned to 8 bins by cost (largest first), and workgroup b takes the next
+// tile of bin b % 8, so the tiles of one matrix share an XCD's L2.
+std::vector<TileWork> order_for_xcds(const std::vector<std::vector<TileWork>>& per_mat,
+                                     const std::vector<double>& cost_per_tile, int n_xcd = 8);
+
+}  // namespace muon

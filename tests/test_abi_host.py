@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is launched).
+
+The library must load, export every function include/libmuon.h declares, and
+validate tables before touching HIP; on a host without a GPU, muon_init must
+fail cleanly with MUON_E_NO_DEVICE.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from muon_newton_schulz_04_amd import binding as B
+from workloads import custom_workload, get_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmuon.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load()
+    names = _declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B._SIGS), "binding and header disagree"
+
+
+def test_struct_sizes_match_c_layout():
+    assert ctypes.sizeof(B.muon_matrix) == 48
+    assert ctypes.sizeof(B.muon_hparams) == 4 * 4 + 16 * 3 * 4 + 4 * 6
+    assert ctypes.sizeof(B.muon_layout) == 8 + 8 + 8 * 4 + 8
+
+
+def test_hparams_default_values():
+    hp = B.muon_hparams_default()
+    assert math.isclose(hp.momentum, 0.95, rel_tol=1e-7)
+    assert hp.nesterov == 1 and hp.ns_steps == 5 and hp.ns_precision == B.MUON_NS_BF16
+    for k in range(B.MUON_MAX_NS_STEPS):
+        a, b, c = hp.ns_coeffs[k]
+        assert (round(a, 4), round(b, 4), round(c, 4)) == (3.4445, -4.775, 2.0315)
+    assert math.isclose(hp.ns_eps, 1e-7, rel_tol=1e-6)
+    assert hp.normuon == 0 and math.isclose(hp.normuon_eps, 1e-10, rel_tol=1e-6)
+
+
+def _ws(entries, hp=None):
+    return B.muon_workspace_bytes(entries, hp)
+
+
+def test_workspace_bytes_arithmetic():
+    # one 100 x 300 matrix (T = 128): canonical 100 x 300 -> padded 128 x 384, bf16
+    w = custom_workload(50, [(100, 300, 1)])
+    s, nbytes = _ws(w.entries, B.muon_hparams_default())
+    assert s == B.MUON_OK
+    x = 128 * 384 * 2
+    a = 128 * 128 * 2
+    assert nbytes >= 3 * x + 2 * a
+    # fp32 mode doubles the Newton-Schulz buffers
+    s2, nbytes32 = _ws(w.entries, B.make_hparams(precision="fp32"))
+    assert s2 == B.MUON_OK and nbytes32 >= 3 * 2 * x + 2 * 2 * a
+    # the 124M body: 48 padded 768^2 + 24 padded 768 x 3072 canonical matrices
+    body = get_workload(1)
+    s3, nb = _ws(body.entries, B.muon_hparams_default())
+    x_elems = 48 * 768 * 768 + 24 * 768 * 3072
+    assert s3 == B.MUON_OK and nb >= 3 * x_elems * 2 + 2 * 72 * 768 * 768 * 2
+
+
+def test_validation_errors():
+    hp = B.muon_hparams_default()
+    M = B.muon_matrix
+    assert _ws([M(0, 4, 1, 0, 1.0, 1.0, 0, 0)], hp)[0] == B.MUON_E_SHAPE
+    assert _ws([M(4, 4, 0, 0, 1.0, 1.0, 0, 0)], hp)[0] == B.MUON_E_SHAPE
+    assert _ws([M(4, 4, 1, -1, 1.0, 1.0, 0, 0)], hp)[0] == B.MUON_E_LAYOUT
+    assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0), M(4, 4, 1, 8, 1.0, 1.0, 0, 0)], hp)[0] == B.MUON_E_LAYOUT
+    assert _ws([M(4, 4, 1, 0, float("nan"), 1.0, 0, 0)], hp)[0] == B.MUON_E_INVALID_ARG
+    assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 7)], hp)[0] == B.MUON_E_INVALID_ARG
+    assert "reserved" in B.muon_last_error()
+    bad = B.muon_hparams_default()
+    bad.ns_steps = 0
+    assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0)], bad)[0] == B.MUON_E_INVALID_ARG
+    bad = B.muon_hparams_default()
+    bad.momentum = 1.5
+    assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0)], bad)[0] == B.MUON_E_INVALID_ARG
+    bad = B.muon_hparams_default()
+    bad.ns_precision = 3
+    assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0)], bad)[0] == B.MUON_E_INVALID_ARG
+    # adjacent (touching) entries are fine; empty table is fine
+    assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0), M(4, 4, 1, 16, 1.0, 1.0, 0, 0)], hp)[0] == B.MUON_OK
+    assert _ws([], hp)[0] == B.MUON_OK
+    # NULL hparams means the defaults
+    assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0)], None)[0] == B.MUON_OK
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert B.muon_status_string(s)
+    assert B.muon_status_string(-99) == "unknown status"
+
+
+def test_init_without_gpu_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host has a GPU")
+    w = custom_workload(51, [(8, 8, 1)])
+    s, nbytes = _ws(w.entries, None)
+    assert s == B.MUON_OK
+    buf = (ctypes.c_ubyte * (nbytes + 256))()
+    addr = (ctypes.addressof(buf) + 255) // 256 * 256
+    s, h = B.muon_init(w.entries, None, addr, nbytes, 0)
+    assert s == B.MUON_E_NO_DEVICE and not h.value
+    # validation comes first: a bad table reports its own error, not the device
+    s, h = B.muon_init([B.muon_matrix(0, 1, 1, 0, 1.0, 1.0, 0, 0)], None, addr, nbytes, 0)
+    assert s == B.MUON_E_SHAPE
+    # a null / misaligned workspace is rejected before the device is queried
+    s, h = B.muon_init(w.entries, None, 0, nbytes, 0)
+    assert s == B.MUON_E_WORKSPACE
+    s, h = B.muon_init(w.entries, None, addr + 16, nbytes, 0)
+    assert s == B.MUON_E_WORKSPACE
+
+
+def test_null_handle_calls_are_safe():
+    lib = B.load()
+    assert lib.muon_step(None, None, None, None, 0, 0.1, -1.0, None) == B.MUON_E_INVALID_ARG
+    assert lib.muon_reset(None, None, 0, None) == B.MUON_E_INVALID_ARG
+    assert lib.muon_num_matrices(None) == 0
+    lib.muon_destroy(None)
