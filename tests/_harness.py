@@ -3,7 +3,7 @@
 Drives libmuon through its C ABI (binding.MuonHandle) on seeded synthetic
 inputs and compares every stage with the CPU oracle, per matrix:
   G1 momentum           (free-running)              rel. Frobenius <= 1e-6
-  G2 X~ = bf16(u)        (vs the oracle's u)         within 1 bf16 ulp
+  G2 X~ = bf16(u)        (u from the GPU's momentum)  within 1 bf16 ulp + fp32 blend error
   G3 Newton-Schulz      (given the GPU's X~ and s)  <= 2e-2 bf16 contract / 1e-4 fp32 vs exact;
      for rank-deficient inputs (contract >5e-2 from exact NS) the 2e-2 gate
      applies to the dominant singular subspace, and the GPU must be no further
@@ -119,15 +119,24 @@ def check_stages(run: GpuRun, step: int, indices, grads_host=None, p_prev=None, 
         orc_m[gi] = m_new
         err = O.rel_fro(run.mat(run.mom, gi), m_new)
         worst["mom"] = max(worst["mom"], err)
-        # G2 X~
+        # G2 X~: the bf16 image of u, with u rebuilt from the GPU's own new
+        # momentum (gated by G1) so only this kernel's arithmetic is tested.
+        # Allowed: one bf16 ulp, plus the float32 forward-error bound of the
+        # blend (1-beta) g + beta m, which matters where the two terms cancel.
         X, tr = O.to_short_side(u)
         xt = run.xtilde(gi)
+        m_gpu = run.mat(run.mom, gi)
+        u_tf = O.nesterov_lerp(g, m_gpu, beta) if w.nesterov else m_gpu
+        bound = 2.0 ** -22 * ((1.0 - beta) * np.abs(g) + beta * np.abs(m_gpu))
+        X_tf, _ = O.to_short_side(u_tf)
+        B_tf, _ = O.to_short_side(bound)
         if run.fp32:
             e2 = O.rel_fro(xt, X)
             assert e2 <= 1e-6, (gi, e2)
+            assert np.all(np.abs(xt - X_tf) <= B_tf + 2.0 ** -24 * np.abs(X_tf)), gi
         else:
-            ref = O.bf16_round(X)
-            viol = np.abs(xt - ref) > O.bf16_ulp(ref)
+            ref = O.bf16_round(X_tf)
+            viol = np.abs(xt - ref) > O.bf16_ulp(ref) + B_tf
             worst["xt_ulp_viol"] += int(viol.sum())
         # G3 NS given the GPU's X~ and s
         s = float(scale[gi])
@@ -179,8 +188,6 @@ def check_stages(run: GpuRun, step: int, indices, grads_host=None, p_prev=None, 
 def assert_worst(worst, fp32=False):
     assert worst["mom"] <= TOL_MOM, worst
     if not fp32:
-        # X~ is the round-to-nearest-even image of u; the GPU's float32 u may sit
-        # on the other side of a rounding boundary, so one ulp is allowed
         assert worst["xt_ulp_viol"] == 0, worst
     assert worst["ns"] <= (TOL_NS_FP32 if fp32 else TOL_NS_BF16), worst
     assert worst.get("ns_ill_signal", 0.0) <= TOL_NS_BF16, worst
