@@ -33,7 +33,7 @@ GRAD_POOL = 4               # distinct gradient sets cycled through the timed st
 
 def _kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("kernels_ns.hip", "kernels_elementwise.hip", "kernel_common.hpp"):
+    for f in ("kernels_ns.hip", "kernels_ns_mfma.hip", "kernels_elementwise.hip", "kernel_common.hpp"):
         with open(os.path.join(ROOT, "muon_newton_schulz_04_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

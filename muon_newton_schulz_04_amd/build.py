@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmuon.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "plan.cpp", "kernels_elementwise.hip", "kernels_ns.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "kernels_elementwise.hip", "kernels_ns.hip", "kernels_ns_mfma.hip"]
 ARCH = "gfx950"
 
 
@@ -35,7 +35,7 @@ def _flags(src: str):
     if src.endswith(".hip"):
         # packed fp32 math stays off; the kernels are written for scalar / float2 code
         return common + ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-                         "-packed-fp32-ops", "-munsafe-fp-atomics"]
+                         "-packed-fp32-ops", "-mllvm", "-disable-promote-alloca-to-lds"]
     return common + [f"--offload-arch={ARCH}"]
 
 

@@ -286,20 +286,16 @@ muon_status muon_step(muon_handle* h, float* params, const float* grads, float* 
         const int rowstats = (k == steps - 1) && P.hp.normuon;
         for (const auto& T : P.lists) {
             const muon::GemmList G = make_list(h, T);
-            s = run(MUON_KERNEL_GRAM, "Gram kernel", [&] {
-                return muon::launch_ns_stage(L, G, muon::NS_GRAM, xin, nullptr, L.a, ca, cb, cc, first,
-                                             P.hp.ns_eps, 0);
-            });
+            const bool big = !L.fp32 && G.T >= 128;
+            auto stage = [&](int mode, const void* x, const void* a, void* o, int rs) {
+                return big ? muon::launch_ns_stage_big(L, G, mode, x, a, o, ca, cb, cc, first, P.hp.ns_eps, rs)
+                           : muon::launch_ns_stage(L, G, mode, x, a, o, ca, cb, cc, first, P.hp.ns_eps, rs);
+            };
+            s = run(MUON_KERNEL_GRAM, "Gram kernel", [&] { return stage(muon::NS_GRAM, xin, nullptr, L.a, 0); });
             if (s != MUON_OK) return s;
-            s = run(MUON_KERNEL_POLY, "polynomial kernel", [&] {
-                return muon::launch_ns_stage(L, G, muon::NS_POLY, nullptr, L.a, L.b, ca, cb, cc, first,
-                                             P.hp.ns_eps, 0);
-            });
+            s = run(MUON_KERNEL_POLY, "polynomial kernel", [&] { return stage(muon::NS_POLY, nullptr, L.a, L.b, 0); });
             if (s != MUON_OK) return s;
-            s = run(MUON_KERNEL_UPDATE, "update kernel", [&] {
-                return muon::launch_ns_stage(L, G, muon::NS_UPDATE, xin, L.b, xout, ca, cb, cc, first,
-                                             P.hp.ns_eps, rowstats);
-            });
+            s = run(MUON_KERNEL_UPDATE, "update kernel", [&] { return stage(muon::NS_UPDATE, xin, L.b, xout, rowstats); });
             if (s != MUON_OK) return s;
         }
     }

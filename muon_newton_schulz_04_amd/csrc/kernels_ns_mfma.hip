@@ -1,0 +1,326 @@
+// bf16 Newton–Schulz stages for the large tiles (T = 128 or 256) on gfx950.
+//
+// Same three stages and epilogues as kernels_ns.hip (Gram with mirrored
+// upper tiles, polynomial epilogue, update with the a X term), re-tiled for
+// MI355X:
+//  * T x T output per 256-thread workgroup, 2 x 2 waves, each wave T/2 x T/2
+//    as (T/64)^2 blocks of v_mfma_f32_32x32x16_bf16 (T = 256: 128 x 128 per
+//    wave, 256 fp32 accumulators per lane), which halves LDS read traffic per
+//    MFMA against 64 x 64 wave tiles.
+//  * K staged in slices of 64 (128 bytes per row) through two LDS buffers;
+//    the next slice is fetched into registers while the current one feeds
+//    the MFMAs.
+//  * Operands whose contraction index is contiguous (rows of X for the
+//    Gram, rows of A, rows of B) sit in LDS as 128-byte rows padded to 144
+//    bytes, so 16 consecutive rows start in 16 distinct 16-byte bank slots.
+//  * The update contracts X over its row index. X stays row-major in LDS
+//    (rows padded to 2T + 64 bytes) and its fragments are read with
+//    ds_read_b64_tr_b16, which hands each lane four consecutive rows of one
+//    column: within a 16-lane group, lane s supplies the address of row
+//    (s >> 2), columns 4 (s & 3) .. +3 of a 4 x 16 block, and lane i receives
+//    column i of that block. Two such reads make one 8-element fragment.
+//  * Every LDS address is a lane base plus a compile-time offset and every
+//    global load is a buffer load with a lane offset and a scalar offset, so
+//    the 256 accumulators leave room for the staged next slice in registers.
+//
+// Source of the iteration: [P4] "modded-nanogpt 50B-token 长时程训练实验解析",
+// section "从源码看 Muon 的分布式正交化实现" (quintic Newton–Schulz in bf16).
+
+#include "kernel_common.hpp"
+#include "launch.hpp"
+
+namespace muon {
+
+namespace {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int BK = 64;       // k per LDS stage
+constexpr int KROW = 144;    // bytes per padded row of a k-contiguous tile (128 + 16)
+
+template <int T>
+struct Layout {
+    static constexpr int XROW = 2 * T + 64;            // bytes per padded row of the X tile
+    static constexpr int KTILE = T * KROW;              // k-contiguous tile, one stage
+    static constexpr int XTILE = BK * XROW;             // X tile, one stage
+    static constexpr int QTILE = KTILE > XTILE ? KTILE : XTILE;
+    static constexpr int STAGE = KTILE + QTILE;
+};
+
+__device__ __forceinline__ bf16x4 tr_read(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(LDS_AS char*)p);
+}
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int T, int MODE>
+__global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__ mats,
+                                                     const TileWork* __restrict__ work, const bf16* __restrict__ xin,
+                                                     const bf16* __restrict__ ain, bf16* __restrict__ out, float ca,
+                                                     float cb, float cc, int first, const float* __restrict__ partials,
+                                                     float* __restrict__ ss_arr, float* __restrict__ scale_arr,
+                                                     int32_t* __restrict__ status_arr, float eps,
+                                                     float* __restrict__ rowpart, int rowstats) {
+    constexpr int WT = T / 2;
+    constexpr int FR = WT / 32;
+    using LY = Layout<T>;
+    constexpr int NCH = T * BK * 2 / 16 / kThreads;  // 16-byte chunks per thread per operand
+    static_assert(NCH >= 1, "tile too small");
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * LY::STAGE];
+    __shared__ float red[4];
+
+    const TileWork w = work[blockIdx.x];
+    const MatDesc d = mats[w.mat];
+    const int i0 = (int)w.ti * T;
+    const int j0 = (int)w.tj * T;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wi = wave >> 1;
+    const int wj = wave & 1;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const bf16* Psrc;
+    const bf16* Qsrc;
+    int ldp, ldq, K;
+    if (MODE == NS_GRAM) {
+        Psrc = xin + d.x_off + (int64_t)i0 * d.n_pad;
+        Qsrc = xin + d.x_off + (int64_t)j0 * d.n_pad;
+        ldp = ldq = d.n_pad;
+        K = d.n_pad;
+    } else if (MODE == NS_POLY) {
+        Psrc = ain + d.a_off + (int64_t)i0 * d.m_pad;
+        Qsrc = ain + d.a_off + (int64_t)j0 * d.m_pad;
+        ldp = ldq = d.m_pad;
+        K = d.m_pad;
+    } else {
+        Psrc = ain + d.a_off + (int64_t)i0 * d.m_pad;  // rows of B
+        Qsrc = xin + d.x_off + j0;                     // columns j0.. of X; row k = contraction
+        ldp = d.m_pad;
+        ldq = d.n_pad;
+        K = d.m_pad;
+    }
+    // buffer ranges: the tile's rows (P, and Q for Gram / poly) or all K rows of X
+    const __amdgpu_buffer_rsrc_t rp = rsrc(Psrc, (uint32_t)(T * ldp * 2));
+    const __amdgpu_buffer_rsrc_t rq =
+        rsrc(Qsrc, (uint32_t)((MODE == NS_UPDATE ? K * ldq : T * ldq) * 2));
+    // lane parts of the global offsets (bytes)
+    const int vp = (tid >> 3) * ldp * 2 + (tid & 7) * 16;
+    const int vq = MODE == NS_UPDATE ? (tid / (T / 8)) * ldq * 2 + (tid % (T / 8)) * 16
+                                     : (tid >> 3) * ldq * 2 + (tid & 7) * 16;
+    // lane parts of the LDS store offsets
+    const int sp = (tid >> 3) * KROW + (tid & 7) * 16;
+    const int sq = MODE == NS_UPDATE ? (tid / (T / 8)) * LY::XROW + (tid % (T / 8)) * 16 : sp;
+
+    uint4 preg[NCH];
+    uint4 qreg[NCH];
+
+    auto load_stage = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) preg[q] = bload(rp, vp, (q * 32 * ldp + k0) * 2);
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            if (MODE != NS_UPDATE)
+                qreg[q] = bload(rq, vq, (q * 32 * ldq + k0) * 2);
+            else
+                qreg[q] = bload(rq, vq, (q * (kThreads / (T / 8)) + k0) * ldq * 2);
+        }
+    };
+
+    auto store_stage = [&](int s) {
+        char* P = smem + s * LY::STAGE;
+        char* Q = P + LY::KTILE;
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) *reinterpret_cast<uint4*>(P + sp + q * 32 * KROW) = preg[q];
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            if (MODE != NS_UPDATE)
+                *reinterpret_cast<uint4*>(Q + sq + q * 32 * KROW) = qreg[q];
+            else
+                *reinterpret_cast<uint4*>(Q + sq + q * (kThreads / (T / 8)) * LY::XROW) = qreg[q];
+        }
+    };
+
+    f32x16 acc[FR][FR];
+#pragma unroll
+    for (int a = 0; a < FR; ++a)
+#pragma unroll
+        for (int b = 0; b < FR; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    // lane bases of the fragment reads
+    const int fp = (wi * WT + l32) * KROW + 16 * hi;          // + f 32 KROW + 32 ks
+    const int fq = (wj * WT + l32) * KROW + 16 * hi;
+    const int g16 = lane >> 4;
+    const int s16 = lane & 15;
+    const int ft = (8 * (g16 >> 1) + (s16 >> 2)) * LY::XROW + 2 * (wj * WT + 16 * (g16 & 1) + 4 * (s16 & 3));
+    // + (16 ks + 4 h) XROW + 64 f
+
+    const int nk = K / BK;
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int s = kt & 1;
+        if (kt + 1 < nk) load_stage((kt + 1) * BK);
+        const char* P = smem + s * LY::STAGE;
+        const char* Q = P + LY::KTILE;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            bf16x8 qf[FR], pf[FR];
+#pragma unroll
+            for (int f = 0; f < FR; ++f) {
+                pf[f] = *reinterpret_cast<const bf16x8*>(P + fp + f * 32 * KROW + 32 * ks);
+                if (MODE != NS_UPDATE) {
+                    qf[f] = *reinterpret_cast<const bf16x8*>(Q + fq + f * 32 * KROW + 32 * ks);
+                } else {
+                    const bf16x4 lo = tr_read(Q + ft + (16 * ks) * LY::XROW + 64 * f);
+                    const bf16x4 up = tr_read(Q + ft + (16 * ks + 4) * LY::XROW + 64 * f);
+                    qf[f] = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            }
+#pragma unroll
+            for (int fi = 0; fi < FR; ++fi)
+#pragma unroll
+                for (int fj = 0; fj < FR; ++fj)
+                    acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[fj], pf[fi], acc[fi][fj], 0, 0, 0);
+            // keep each k16 sub-step's fragments from being hoisted into the previous one
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kt + 1 < nk) store_stage(s ^ 1);
+        __syncthreads();
+    }
+
+    // ---------------- epilogue (lane holds C[i][j .. j+3]) ----------------
+    float alpha = 1.0f;
+    if (MODE == NS_GRAM && first) {
+        float acc_p = 0.f;
+        for (int p = tid; p < d.ew_count; p += kThreads) acc_p += partials[d.ew_start + p];
+        const float total = block_sum_256(acc_p, red);
+        const float sc = 1.0f / (sqrtf(total) + eps);
+        alpha = sc * sc;
+        if (w.ti == 0 && w.tj == 0 && tid == 0) {
+            ss_arr[w.mat] = total;
+            scale_arr[w.mat] = sc;
+            status_arr[w.mat] = (isfinite(total) ? 0 : 1);
+        }
+    }
+    if (MODE == NS_UPDATE && first) alpha = scale_arr[w.mat];
+    const float xa = ca * alpha;
+
+    float rsq[FR];
+#pragma unroll
+    for (int f = 0; f < FR; ++f) rsq[f] = 0.f;
+
+#pragma unroll
+    for (int fi = 0; fi < FR; ++fi) {
+        const int i = i0 + wi * WT + fi * 32 + l32;
+#pragma unroll
+        for (int fj = 0; fj < FR; ++fj) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int jb = j0 + wj * WT + fj * 32 + 8 * g + 4 * hi;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[fi][fj][4 * g + e];
+                if (MODE == NS_UPDATE) {
+                    const uint2 xw = *reinterpret_cast<const uint2*>(xin + d.x_off + (int64_t)i * d.n_pad + jb);
+                    v[0] = fmaf(xa, bf16_lo(xw.x), alpha * v[0]);
+                    v[1] = fmaf(xa, bf16_hi(xw.x), alpha * v[1]);
+                    v[2] = fmaf(xa, bf16_lo(xw.y), alpha * v[2]);
+                    v[3] = fmaf(xa, bf16_hi(xw.y), alpha * v[3]);
+                } else if (MODE == NS_POLY) {
+                    const uint2 aw = *reinterpret_cast<const uint2*>(ain + d.a_off + (int64_t)i * d.m_pad + jb);
+                    v[0] = fmaf(cb, bf16_lo(aw.x), cc * v[0]);
+                    v[1] = fmaf(cb, bf16_hi(aw.x), cc * v[1]);
+                    v[2] = fmaf(cb, bf16_lo(aw.y), cc * v[2]);
+                    v[3] = fmaf(cb, bf16_hi(aw.y), cc * v[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] *= alpha;
+                }
+                uint2 ow;
+                ow.x = pack_bf16x2(v[0], v[1]);
+                ow.y = pack_bf16x2(v[2], v[3]);
+                if (MODE == NS_UPDATE) {
+                    *reinterpret_cast<uint2*>(out + d.x_off + (int64_t)i * d.n_pad + jb) = ow;
+                    if (rowstats) {
+                        const float r0 = bf16_lo(ow.x), r1 = bf16_hi(ow.x), r2 = bf16_lo(ow.y), r3 = bf16_hi(ow.y);
+                        rsq[fi] = fmaf(r0, r0, rsq[fi]);
+                        rsq[fi] = fmaf(r1, r1, rsq[fi]);
+                        rsq[fi] = fmaf(r2, r2, rsq[fi]);
+                        rsq[fi] = fmaf(r3, r3, rsq[fi]);
+                    }
+                } else {
+                    bf16* o = out + d.a_off;
+                    *reinterpret_cast<uint2*>(o + (int64_t)i * d.m_pad + jb) = ow;
+                    if (w.ti != w.tj) {
+                        uint16_t* om = reinterpret_cast<uint16_t*>(o);
+                        om[(int64_t)(jb + 0) * d.m_pad + i] = (uint16_t)(ow.x & 0xffffu);
+                        om[(int64_t)(jb + 1) * d.m_pad + i] = (uint16_t)(ow.x >> 16);
+                        om[(int64_t)(jb + 2) * d.m_pad + i] = (uint16_t)(ow.y & 0xffffu);
+                        om[(int64_t)(jb + 3) * d.m_pad + i] = (uint16_t)(ow.y >> 16);
+                    }
+                }
+            }
+        }
+    }
+
+    if (MODE == NS_UPDATE && rowstats) {
+        float* rl = reinterpret_cast<float*>(smem);  // [2 wi][2 wj][WT]
+#pragma unroll
+        for (int f = 0; f < FR; ++f) rsq[f] += __shfl_xor(rsq[f], 32, 64);
+        if (hi == 0) {
+#pragma unroll
+            for (int f = 0; f < FR; ++f) rl[(wi * 2 + wj) * WT + f * 32 + l32] = rsq[f];
+        }
+        __syncthreads();
+        if (tid < T) {
+            const int wr = tid / WT;
+            const int rr = tid % WT;
+            const float sum = rl[(wr * 2 + 0) * WT + rr] + rl[(wr * 2 + 1) * WT + rr];
+            rowpart[d.rowpart_off + (int64_t)w.tj * d.m_pad + i0 + tid] = sum;
+        }
+    }
+}
+
+template <int T>
+hipError_t launch_big_T(const LaunchCtx& L, const GemmList& G, int mode, const void* xin, const void* ain, void* out,
+                        float ca, float cb, float cc, int first, float eps, int rowstats) {
+    const TileWork* wl = mode == NS_GRAM ? G.gram : mode == NS_POLY ? G.poly : G.update;
+    const int n = mode == NS_GRAM ? G.n_gram : mode == NS_POLY ? G.n_poly : G.n_update;
+    if (n == 0) return hipSuccess;
+    const bf16* x = (const bf16*)xin;
+    const bf16* a = (const bf16*)ain;
+    bf16* o = (bf16*)out;
+    if (mode == NS_GRAM)
+        k_ns_big<T, NS_GRAM><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials, L.ss,
+                                                           L.scale, L.status, eps, L.rowpart, rowstats);
+    else if (mode == NS_POLY)
+        k_ns_big<T, NS_POLY><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials, L.ss,
+                                                           L.scale, L.status, eps, L.rowpart, rowstats);
+    else
+        k_ns_big<T, NS_UPDATE><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials,
+                                                             L.ss, L.scale, L.status, eps, L.rowpart, rowstats);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ns_stage_big(const LaunchCtx& L, const GemmList& G, int mode, const void* xin, const void* ain,
+                               void* out, float ca, float cb, float cc, int first, float eps, int rowstats) {
+    if (G.T == 256) return launch_big_T<256>(L, G, mode, xin, ain, out, ca, cb, cc, first, eps, rowstats);
+    return launch_big_T<128>(L, G, mode, xin, ain, out, ca, cb, cc, first, eps, rowstats);
+}
+
+}  // namespace muon

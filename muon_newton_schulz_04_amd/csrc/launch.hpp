@@ -60,4 +60,8 @@ hipError_t launch_reset(const LaunchCtx& L, float* mom);
 hipError_t launch_ns_stage(const LaunchCtx& L, const GemmList& G, int mode, const void* xin, const void* ain,
                            void* out, float ca, float cb, float cc, int first, float eps, int rowstats);
 
+// The same stage with the bf16 large-tile kernels (T = 128 or 256).
+hipError_t launch_ns_stage_big(const LaunchCtx& L, const GemmList& G, int mode, const void* xin, const void* ain,
+                               void* out, float ca, float cb, float cc, int first, float eps, int rowstats);
+
 }  // namespace muon

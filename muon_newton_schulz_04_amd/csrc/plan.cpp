@@ -25,6 +25,14 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 bool finite(float x) { return std::isfinite(x); }
 
+// GEMM tile for a matrix whose short side is m: 256 where it adds no padding
+// beyond what 128 would (large matrices, bf16 only), 128 for medium, 64 small.
+int pick_tile(int64_t m, bool fp32) {
+    if (m <= 64) return 64;
+    if (!fp32 && m >= 384 && round_up(m, 256) <= round_up(m, 128) + m / 32) return 256;
+    return 128;
+}
+
 }  // namespace
 
 muon_status check_hparams(const muon_hparams* hp, std::string* err) {
@@ -175,10 +183,10 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
             d.transposed = t.rows > t.cols ? 1 : 0;
             d.m = (int32_t)std::min(t.rows, t.cols);
             d.n = (int32_t)std::max(t.rows, t.cols);
-            d.T = d.m <= 64 ? 64 : 128;
+            d.T = pick_tile(d.m, P.hp.ns_precision == MUON_NS_FP32);
             d.m_pad = (int32_t)round_up(d.m, d.T);
             d.n_pad = (int32_t)round_up(d.n, d.T);
-            if ((int64_t)d.m_pad * d.n_pad >= (INT64_C(1) << 31)) {
+            if ((int64_t)d.m_pad * d.n_pad >= (INT64_C(1) << 30)) {
                 *err = "entry " + std::to_string(e) + ": matrix too large for one tile grid";
                 return MUON_E_SHAPE;
             }
@@ -217,7 +225,7 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
         for (int t = 0; t < P.mats[mi].ew_count; ++t) P.ew_map.push_back(mi);
 
     // ---- GEMM work lists per tile size ----
-    for (int T : {128, 64}) {
+    for (int T : {256, 128, 64}) {
         std::vector<std::vector<TileWork>> g, u;
         std::vector<double> cg, cp, cu;
         for (int32_t mi : P.active) {

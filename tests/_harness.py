@@ -126,8 +126,10 @@ def check_stages(run: GpuRun, step: int, indices, grads_host=None, p_prev=None, 
         X, tr = O.to_short_side(u)
         xt = run.xtilde(gi)
         m_gpu = run.mat(run.mom, gi)
-        u_tf = O.nesterov_lerp(g, m_gpu, beta) if w.nesterov else m_gpu
-        bound = 2.0 ** -22 * ((1.0 - beta) * np.abs(g) + beta * np.abs(m_gpu))
+        b32 = float(np.float32(beta))             # the ABI passes beta as float32
+        c32 = float(np.float32(1.0) - np.float32(beta))
+        u_tf = c32 * g + b32 * m_gpu if w.nesterov else m_gpu
+        bound = 2.0 ** -23 * (c32 * np.abs(g) + b32 * np.abs(m_gpu))
         X_tf, _ = O.to_short_side(u_tf)
         B_tf, _ = O.to_short_side(bound)
         if run.fp32:
