@@ -1,15 +1,16 @@
 // bf16 Newton–Schulz stages for the large tiles (T = 128 or 256) on gfx950.
 //
-// Same three stages and epilogues as kernels_ns.hip (Gram with mirrored
-// upper tiles, polynomial epilogue, update with the a X term), re-tiled for
-// MI355X:
+// Same three stages as kernels_ns.hip (Gram with mirrored upper tiles,
+// polynomial epilogue, update), re-tiled for MI355X:
 //  * T x T output per 256-thread workgroup, 2 x 2 waves, each wave T/2 x T/2
 //    as (T/64)^2 blocks of v_mfma_f32_32x32x16_bf16 (T = 256: 128 x 128 per
 //    wave, 256 fp32 accumulators per lane), which halves LDS read traffic per
 //    MFMA against 64 x 64 wave tiles.
 //  * K staged in slices of 64 (128 bytes per row) through two LDS buffers;
 //    the next slice is fetched into registers while the current one feeds
-//    the MFMAs.
+//    the MFMAs: its global loads are interleaved one per MFMA over the first
+//    two k16 sub-steps and written to LDS in the last, and the fragment reads
+//    of sub-step k+1 run under the MFMAs of sub-step k.
 //  * Operands whose contraction index is contiguous (rows of X for the
 //    Gram, rows of A, rows of B) sit in LDS as 128-byte rows padded to 144
 //    bytes, so 16 consecutive rows start in 16 distinct 16-byte bank slots.
@@ -19,12 +20,17 @@
 //    column: within a 16-lane group, lane s supplies the address of row
 //    (s >> 2), columns 4 (s & 3) .. +3 of a 4 x 16 block, and lane i receives
 //    column i of that block. Two such reads make one 8-element fragment.
+//  * The a X term of the update is folded into the polynomial: the poly
+//    kernel writes B' = a I + b A + c A A, so the update is the pure product
+//    X' = alpha B' X and reads X once per iteration.
 //  * Every LDS address is a lane base plus a compile-time offset and every
 //    global load is a buffer load with a lane offset and a scalar offset, so
 //    the 256 accumulators leave room for the staged next slice in registers.
 //
 // Source of the iteration: [P4] "modded-nanogpt 50B-token 长时程训练实验解析",
 // section "从源码看 Muon 的分布式正交化实现" (quintic Newton–Schulz in bf16).
+
+#include <type_traits>
 
 #include "kernel_common.hpp"
 #include "launch.hpp"
@@ -60,14 +66,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int T, int MODE>
+template <int T, int MODE, bool ROWSTATS>
 __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__ mats,
                                                      const TileWork* __restrict__ work, const bf16* __restrict__ xin,
                                                      const bf16* __restrict__ ain, bf16* __restrict__ out, float ca,
                                                      float cb, float cc, int first, const float* __restrict__ partials,
                                                      float* __restrict__ ss_arr, float* __restrict__ scale_arr,
                                                      int32_t* __restrict__ status_arr, float eps,
-                                                     float* __restrict__ rowpart, int rowstats) {
+                                                     float* __restrict__ rowpart) {
     constexpr int WT = T / 2;
     constexpr int FR = WT / 32;
     using LY = Layout<T>;
@@ -124,15 +130,20 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
     uint4 preg[NCH];
     uint4 qreg[NCH];
 
-    auto load_stage = [&](int k0) {
+    // global -> registers for one stage; which = 1: P chunks, 2: Q chunks, 3: both
+    auto load_stage = [&](int k0, int which) {
+        if (which & 1) {
 #pragma unroll
-        for (int q = 0; q < NCH; ++q) preg[q] = bload(rp, vp, (q * 32 * ldp + k0) * 2);
+            for (int q = 0; q < NCH; ++q) preg[q] = bload(rp, vp, (q * 32 * ldp + k0) * 2);
+        }
+        if (which & 2) {
 #pragma unroll
-        for (int q = 0; q < NCH; ++q) {
-            if (MODE != NS_UPDATE)
-                qreg[q] = bload(rq, vq, (q * 32 * ldq + k0) * 2);
-            else
-                qreg[q] = bload(rq, vq, (q * (kThreads / (T / 8)) + k0) * ldq * 2);
+            for (int q = 0; q < NCH; ++q) {
+                if (MODE != NS_UPDATE)
+                    qreg[q] = bload(rq, vq, (q * 32 * ldq + k0) * 2);
+                else
+                    qreg[q] = bload(rq, vq, (q * (kThreads / (T / 8)) + k0) * ldq * 2);
+            }
         }
     };
 
@@ -166,40 +177,68 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
     const int ft = (8 * (g16 >> 1) + (s16 >> 2)) * LY::XROW + 2 * (wj * WT + 16 * (g16 & 1) + 4 * (s16 & 3));
     // + (16 ks + 4 h) XROW + 64 f
 
-    const int nk = K / BK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int s = kt & 1;
-        if (kt + 1 < nk) load_stage((kt + 1) * BK);
-        const char* P = smem + s * LY::STAGE;
+    // two fragment sets, alternating between k16 sub-steps
+    bf16x8 pfr[2][FR], qfr[2][FR];
+    auto read_frags = [&](const char* P, int ks, int set) {
         const char* Q = P + LY::KTILE;
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 qf[FR], pf[FR];
+        for (int f = 0; f < FR; ++f) {
+            pfr[set][f] = *reinterpret_cast<const bf16x8*>(P + fp + f * 32 * KROW + 32 * ks);
+            if (MODE != NS_UPDATE) {
+                qfr[set][f] = *reinterpret_cast<const bf16x8*>(Q + fq + f * 32 * KROW + 32 * ks);
+            } else {
+                const bf16x4 lo = tr_read(Q + ft + (16 * ks) * LY::XROW + 64 * f);
+                const bf16x4 up = tr_read(Q + ft + (16 * ks + 4) * LY::XROW + 64 * f);
+                qfr[set][f] = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+    };
+    constexpr int NREAD = MODE == NS_UPDATE ? 3 * FR : 2 * FR;  // LDS read instructions per sub-step
+
+    // One K stage. MORE: a next stage exists (its loads and LDS writes are
+    // interleaved here); the last stage is peeled so the steady-state loop
+    // body has no branches for the scheduler to stop at.
+    auto stage = [&](int kt, auto more_c) {
+        constexpr bool MORE = decltype(more_c)::value;
+        const char* P = smem + (kt & 1) * LY::STAGE;
 #pragma unroll
-            for (int f = 0; f < FR; ++f) {
-                pf[f] = *reinterpret_cast<const bf16x8*>(P + fp + f * 32 * KROW + 32 * ks);
-                if (MODE != NS_UPDATE) {
-                    qf[f] = *reinterpret_cast<const bf16x8*>(Q + fq + f * 32 * KROW + 32 * ks);
-                } else {
-                    const bf16x4 lo = tr_read(Q + ft + (16 * ks) * LY::XROW + 64 * f);
-                    const bf16x4 up = tr_read(Q + ft + (16 * ks + 4) * LY::XROW + 64 * f);
-                    qf[f] = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int set = ks & 1;
+            if (ks + 1 < BK / 16) read_frags(P, ks + 1, set ^ 1);
+            // the next stage's global loads are spread over sub-steps 0 and 1
+            // (one per MFMA) and land in the other LDS buffer in sub-step 3
+            if constexpr (MORE) {
+                if (ks == 0) load_stage((kt + 1) * BK, 1);
+                if (ks == 1) load_stage((kt + 1) * BK, 2);
+                if (ks == 3) store_stage((kt & 1) ^ 1);
             }
 #pragma unroll
             for (int fi = 0; fi < FR; ++fi)
 #pragma unroll
                 for (int fj = 0; fj < FR; ++fj)
-                    acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[fj], pf[fi], acc[fi][fj], 0, 0, 0);
-            // keep each k16 sub-step's fragments from being hoisted into the previous one
-            __builtin_amdgcn_sched_barrier(0);
+                    acc[fi][fj] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[set][fj], pfr[set][fi], acc[fi][fj], 0, 0, 0);
+            // interleave: one MFMA, then one LDS read / global load / LDS write
+            constexpr int NW = 2 * NCH;
+#pragma unroll
+            for (int i = 0; i < FR * FR; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (ks + 1 < BK / 16 && i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (MORE && ks < 2 && i < NCH) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (MORE && ks == 3 && i < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            }
         }
-        if (kt + 1 < nk) store_stage(s ^ 1);
         __syncthreads();
-    }
+        if constexpr (MORE) read_frags(smem + ((kt + 1) & 1) * LY::STAGE, 0, 0);
+    };
+
+    const int nk = K / BK;
+    load_stage(0, 3);
+    store_stage(0);
+    __syncthreads();
+    read_frags(smem, 0, 0);
+    for (int kt = 0; kt < nk - 1; ++kt) stage(kt, std::true_type{});
+    stage(nk - 1, std::false_type{});
 
     // ---------------- epilogue (lane holds C[i][j .. j+3]) ----------------
     float alpha = 1.0f;
@@ -216,35 +255,60 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
         }
     }
     if (MODE == NS_UPDATE && first) alpha = scale_arr[w.mat];
-    const float xa = ca * alpha;
+
+    // The polynomial needs A[i][j] of its own output tile: stage that tile
+    // through the (now idle) LDS with coalesced 16-byte loads, NCH per batch.
+    constexpr int EROW = 2 * T + 16;                 // bytes per staged row
+    if (MODE == NS_POLY) {
+        static_assert(T * EROW <= 2 * LY::STAGE, "staged A tile must fit in LDS");
+        const bf16* Asrc = ain + d.a_off + (int64_t)i0 * d.m_pad + j0;
+        const __amdgpu_buffer_rsrc_t ra = rsrc(Asrc, (uint32_t)(T * d.m_pad * 2));
+        constexpr int CPR = T / 8;                   // 16-byte chunks per row
+        constexpr int NE = T * CPR / kThreads;       // chunks per thread
+        const int er = tid / CPR, ec = tid % CPR;    // row / chunk of this thread's first chunk
+        constexpr int RSTEP = kThreads / CPR;        // rows between a thread's chunks
+#pragma unroll
+        for (int b0 = 0; b0 < NE; b0 += NCH) {
+#pragma unroll
+            for (int q = 0; q < NCH; ++q)
+                preg[q] = bload(ra, er * d.m_pad * 2 + ec * 16, (b0 + q) * RSTEP * d.m_pad * 2);
+#pragma unroll
+            for (int q = 0; q < NCH; ++q)
+                *reinterpret_cast<uint4*>(smem + (er + (b0 + q) * RSTEP) * EROW + ec * 16) = preg[q];
+        }
+        __syncthreads();
+    }
 
     float rsq[FR];
 #pragma unroll
     for (int f = 0; f < FR; ++f) rsq[f] = 0.f;
 
+    uint2 ev[FR][FR][4];
 #pragma unroll
     for (int fi = 0; fi < FR; ++fi) {
-        const int i = i0 + wi * WT + fi * 32 + l32;
+        const int il = wi * WT + fi * 32 + l32;
+        const int i = i0 + il;
 #pragma unroll
         for (int fj = 0; fj < FR; ++fj) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int jb = j0 + wj * WT + fj * 32 + 8 * g + 4 * hi;
+                const int jl = wj * WT + fj * 32 + 8 * g + 4 * hi;
+                const int jb = j0 + jl;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[fi][fj][4 * g + e];
-                if (MODE == NS_UPDATE) {
-                    const uint2 xw = *reinterpret_cast<const uint2*>(xin + d.x_off + (int64_t)i * d.n_pad + jb);
-                    v[0] = fmaf(xa, bf16_lo(xw.x), alpha * v[0]);
-                    v[1] = fmaf(xa, bf16_hi(xw.x), alpha * v[1]);
-                    v[2] = fmaf(xa, bf16_lo(xw.y), alpha * v[2]);
-                    v[3] = fmaf(xa, bf16_hi(xw.y), alpha * v[3]);
-                } else if (MODE == NS_POLY) {
-                    const uint2 aw = *reinterpret_cast<const uint2*>(ain + d.a_off + (int64_t)i * d.m_pad + jb);
-                    v[0] = fmaf(cb, bf16_lo(aw.x), cc * v[0]);
-                    v[1] = fmaf(cb, bf16_hi(aw.x), cc * v[1]);
-                    v[2] = fmaf(cb, bf16_lo(aw.y), cc * v[2]);
-                    v[3] = fmaf(cb, bf16_hi(aw.y), cc * v[3]);
+                if (MODE == NS_POLY) {
+                    // B' = a I + b A + c A A: the a X term of the update rides on B's diagonal
+                    const uint2 in = *reinterpret_cast<const uint2*>(smem + il * EROW + 2 * jl);
+                    v[0] = fmaf(cb, bf16_lo(in.x), cc * v[0]);
+                    v[1] = fmaf(cb, bf16_hi(in.x), cc * v[1]);
+                    v[2] = fmaf(cb, bf16_lo(in.y), cc * v[2]);
+                    v[3] = fmaf(cb, bf16_hi(in.y), cc * v[3]);
+                    if (w.ti == w.tj) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (jb + e == i) v[e] += ca;
+                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] *= alpha;
@@ -252,9 +316,10 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
                 uint2 ow;
                 ow.x = pack_bf16x2(v[0], v[1]);
                 ow.y = pack_bf16x2(v[2], v[3]);
+                ev[fi][fj][g] = ow;
                 if (MODE == NS_UPDATE) {
                     *reinterpret_cast<uint2*>(out + d.x_off + (int64_t)i * d.n_pad + jb) = ow;
-                    if (rowstats) {
+                    if (ROWSTATS) {
                         const float r0 = bf16_lo(ow.x), r1 = bf16_hi(ow.x), r2 = bf16_lo(ow.y), r3 = bf16_hi(ow.y);
                         rsq[fi] = fmaf(r0, r0, rsq[fi]);
                         rsq[fi] = fmaf(r1, r1, rsq[fi]);
@@ -262,21 +327,33 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
                         rsq[fi] = fmaf(r3, r3, rsq[fi]);
                     }
                 } else {
-                    bf16* o = out + d.a_off;
-                    *reinterpret_cast<uint2*>(o + (int64_t)i * d.m_pad + jb) = ow;
-                    if (w.ti != w.tj) {
-                        uint16_t* om = reinterpret_cast<uint16_t*>(o);
-                        om[(int64_t)(jb + 0) * d.m_pad + i] = (uint16_t)(ow.x & 0xffffu);
-                        om[(int64_t)(jb + 1) * d.m_pad + i] = (uint16_t)(ow.x >> 16);
-                        om[(int64_t)(jb + 2) * d.m_pad + i] = (uint16_t)(ow.y & 0xffffu);
-                        om[(int64_t)(jb + 3) * d.m_pad + i] = (uint16_t)(ow.y >> 16);
-                    }
+                    *reinterpret_cast<uint2*>(out + d.a_off + (int64_t)i * d.m_pad + jb) = ow;
                 }
             }
         }
     }
+    if (MODE != NS_UPDATE && w.ti != w.tj) {
+        // mirror tile: the transposed entries, 2 bytes each; for fixed (fj, g, e)
+        // the 32 lanes of a half-wave write 64 contiguous bytes of one row
+        uint16_t* om = reinterpret_cast<uint16_t*>(out + d.a_off);
+#pragma unroll
+        for (int fi = 0; fi < FR; ++fi) {
+            const int i = i0 + wi * WT + fi * 32 + l32;
+#pragma unroll
+            for (int fj = 0; fj < FR; ++fj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int jb = j0 + wj * WT + fj * 32 + 8 * g + 4 * hi;
+                    const uint2 ow = ev[fi][fj][g];
+                    om[(int64_t)(jb + 0) * d.m_pad + i] = (uint16_t)(ow.x & 0xffffu);
+                    om[(int64_t)(jb + 1) * d.m_pad + i] = (uint16_t)(ow.x >> 16);
+                    om[(int64_t)(jb + 2) * d.m_pad + i] = (uint16_t)(ow.y & 0xffffu);
+                    om[(int64_t)(jb + 3) * d.m_pad + i] = (uint16_t)(ow.y >> 16);
+                }
+        }
+    }
 
-    if (MODE == NS_UPDATE && rowstats) {
+    if (MODE == NS_UPDATE && ROWSTATS) {
         float* rl = reinterpret_cast<float*>(smem);  // [2 wi][2 wj][WT]
 #pragma unroll
         for (int f = 0; f < FR; ++f) rsq[f] += __shfl_xor(rsq[f], 32, 64);
@@ -304,14 +381,18 @@ hipError_t launch_big_T(const LaunchCtx& L, const GemmList& G, int mode, const v
     const bf16* a = (const bf16*)ain;
     bf16* o = (bf16*)out;
     if (mode == NS_GRAM)
-        k_ns_big<T, NS_GRAM><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials, L.ss,
-                                                           L.scale, L.status, eps, L.rowpart, rowstats);
+        k_ns_big<T, NS_GRAM, false><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials,
+                                                                  L.ss, L.scale, L.status, eps, L.rowpart);
     else if (mode == NS_POLY)
-        k_ns_big<T, NS_POLY><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials, L.ss,
-                                                           L.scale, L.status, eps, L.rowpart, rowstats);
+        k_ns_big<T, NS_POLY, false><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials,
+                                                                  L.ss, L.scale, L.status, eps, L.rowpart);
+    else if (rowstats)
+        k_ns_big<T, NS_UPDATE, true><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first,
+                                                                   L.partials, L.ss, L.scale, L.status, eps, L.rowpart);
     else
-        k_ns_big<T, NS_UPDATE><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials,
-                                                             L.ss, L.scale, L.status, eps, L.rowpart, rowstats);
+        k_ns_big<T, NS_UPDATE, false><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first,
+                                                                    L.partials, L.ss, L.scale, L.status, eps,
+                                                                    L.rowpart);
     return hipGetLastError();
 }
 

@@ -28,8 +28,9 @@ Readings where the pages are silent or garbled (each listed in the design doc):
      NS runs on X = u^T when rows > cols, so that X has rows <= cols.
   R4 s = 1/(||u||_F + 1e-7) from the float u; in the bf16 rounding contract
      s is folded into iteration 0 instead of rounding s*X to bf16.
-  R5 The bf16 rounding contract: four rounding points per iteration (the bf16
-     outputs X~, A, B, X), each product accumulated exactly (float64 here).
+  R5 The bf16 rounding contract: the input X~ is rounded once, then three
+     rounding points per iteration (the bf16 outputs A, P = a I + b A + c A^2
+     and X = P X), each product accumulated exactly (float64 here).
   R6 NorMuon per row of the canonical (rows <= cols) frame: mean of squares
      over the longer dimension, v EMA with v0 = 0 and no bias correction,
      divide by sqrt(v)+eps, rescale to keep the Frobenius norm, 0/0 -> 0.
@@ -149,24 +150,27 @@ def ns_exact_factored(X, s: float, coeffs=None) -> np.ndarray:
 def ns_bf16_contract(Xt, s: float, coeffs=None) -> np.ndarray:
     """bf16 rounding contract of the factored iteration (readings R4, R5).
 
-    Xt: the bf16-rounded short-side input (float64 array of bf16 values);
-    s: the normalising factor, folded into iteration 0. Products are exact
-    (float64); R() rounds to bf16 at the four fixed points:
-      it 0:  A = R(s^2 Xt Xt^T);  B = R(b A + c A A);  X = R(a s Xt + s B Xt)
-      it>0:  A = R(X X^T);        B = R(b A + c A A);  X = R(a X + B X)
+    The quintic step X <- a X + b (X X^T) X + c (X X^T)^2 X is the matrix
+    polynomial (a I + b A + c A^2) applied to X, A = X X^T. Xt: the
+    bf16-rounded short-side input (float64 array of bf16 values); s: the
+    normalising factor, folded into iteration 0. Products are exact (float64);
+    R() rounds to bf16 at three points per iteration:
+      it 0:  A = R(s^2 Xt Xt^T);  P = R(a I + b A + c A A);  X = R(s P Xt)
+      it>0:  A = R(X X^T);        P = R(a I + b A + c A A);  X = R(P X)
     """
     coeffs = default_coeffs() if coeffs is None else coeffs
     X = np.asarray(Xt, np.float64)
+    eye = np.eye(X.shape[0])
     for k, (a, b, c) in enumerate(coeffs):
         if k == 0:
             A = bf16_round((s * s) * (X @ X.T))
         else:
             A = bf16_round(X @ X.T)
-        B = bf16_round(b * A + c * (A @ A))
+        P = bf16_round(a * eye + b * A + c * (A @ A))
         if k == 0:
-            X = bf16_round(a * s * X + s * (B @ X))
+            X = bf16_round(s * (P @ X))
         else:
-            X = bf16_round(a * X + B @ X)
+            X = bf16_round(P @ X)
     return X
 
 

@@ -171,8 +171,8 @@ def test_bf16_contract_diagonal_recurrence():
         x = float(xt[i, i])
         for k in range(5):
             A = _bf16_torch((s * s) * (x * x)) if k == 0 else _bf16_torch(x * x)
-            B = _bf16_torch(b * A + c * (A * A))
-            x = _bf16_torch(a * s * x + s * (B * x)) if k == 0 else _bf16_torch(a * x + B * x)
+            P = _bf16_torch(a + b * A + c * (A * A))
+            x = _bf16_torch(s * (P * x)) if k == 0 else _bf16_torch(P * x)
         assert abs(out[i, i] - x) <= O.bf16_ulp(x), (i, out[i, i], x)
     off = out.copy()
     off[np.arange(m), np.arange(m)] = 0
