@@ -256,25 +256,31 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
     }
     if (MODE == NS_UPDATE && first) alpha = scale_arr[w.mat];
 
-    // The polynomial needs A[i][j] of its own output tile: stage that tile
-    // through the (now idle) LDS with coalesced 16-byte loads, NCH per batch.
-    constexpr int EROW = 2 * T + 16;                 // bytes per staged row
+    // Output tiles are staged in LDS as bf16 rows of EROW bytes (2T + 8: 32
+    // consecutive rows start in distinct 8-byte bank slots) and leave as
+    // whole cache lines; the polynomial's A tile comes in the same way.
+    constexpr int EROW = 2 * T + 8;
+    static_assert(T * EROW <= 2 * LY::STAGE, "staged tile must fit in LDS");
+    auto lds64 = [&](int off) -> uint2& { return *reinterpret_cast<uint2*>(smem + off); };
+
     if (MODE == NS_POLY) {
-        static_assert(T * EROW <= 2 * LY::STAGE, "staged A tile must fit in LDS");
         const bf16* Asrc = ain + d.a_off + (int64_t)i0 * d.m_pad + j0;
         const __amdgpu_buffer_rsrc_t ra = rsrc(Asrc, (uint32_t)(T * d.m_pad * 2));
         constexpr int CPR = T / 8;                   // 16-byte chunks per row
         constexpr int NE = T * CPR / kThreads;       // chunks per thread
-        const int er = tid / CPR, ec = tid % CPR;    // row / chunk of this thread's first chunk
-        constexpr int RSTEP = kThreads / CPR;        // rows between a thread's chunks
+        const int er = tid / CPR, ec = tid % CPR;
+        constexpr int RSTEP = kThreads / CPR;
 #pragma unroll
         for (int b0 = 0; b0 < NE; b0 += NCH) {
 #pragma unroll
             for (int q = 0; q < NCH; ++q)
                 preg[q] = bload(ra, er * d.m_pad * 2 + ec * 16, (b0 + q) * RSTEP * d.m_pad * 2);
 #pragma unroll
-            for (int q = 0; q < NCH; ++q)
-                *reinterpret_cast<uint4*>(smem + (er + (b0 + q) * RSTEP) * EROW + ec * 16) = preg[q];
+            for (int q = 0; q < NCH; ++q) {
+                const int off = (er + (b0 + q) * RSTEP) * EROW + ec * 16;
+                lds64(off) = make_uint2(preg[q].x, preg[q].y);
+                lds64(off + 8) = make_uint2(preg[q].z, preg[q].w);
+            }
         }
         __syncthreads();
     }
@@ -287,19 +293,17 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
 #pragma unroll
     for (int fi = 0; fi < FR; ++fi) {
         const int il = wi * WT + fi * 32 + l32;
-        const int i = i0 + il;
 #pragma unroll
         for (int fj = 0; fj < FR; ++fj) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int jl = wj * WT + fj * 32 + 8 * g + 4 * hi;
-                const int jb = j0 + jl;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[fi][fj][4 * g + e];
                 if (MODE == NS_POLY) {
-                    // B' = a I + b A + c A A: the a X term of the update rides on B's diagonal
-                    const uint2 in = *reinterpret_cast<const uint2*>(smem + il * EROW + 2 * jl);
+                    // P = a I + b A + c A A: the a X term of the update rides on P's diagonal
+                    const uint2 in = lds64(il * EROW + 2 * jl);
                     v[0] = fmaf(cb, bf16_lo(in.x), cc * v[0]);
                     v[1] = fmaf(cb, bf16_hi(in.x), cc * v[1]);
                     v[2] = fmaf(cb, bf16_lo(in.y), cc * v[2]);
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
                     if (w.ti == w.tj) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (jb + e == i) v[e] += ca;
+                            if (jl + e == il) v[e] += ca;
                     }
                 } else {
 #pragma unroll
@@ -317,43 +321,64 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
                 ow.x = pack_bf16x2(v[0], v[1]);
                 ow.y = pack_bf16x2(v[2], v[3]);
                 ev[fi][fj][g] = ow;
-                if (MODE == NS_UPDATE) {
-                    *reinterpret_cast<uint2*>(out + d.x_off + (int64_t)i * d.n_pad + jb) = ow;
-                    if (ROWSTATS) {
-                        const float r0 = bf16_lo(ow.x), r1 = bf16_hi(ow.x), r2 = bf16_lo(ow.y), r3 = bf16_hi(ow.y);
-                        rsq[fi] = fmaf(r0, r0, rsq[fi]);
-                        rsq[fi] = fmaf(r1, r1, rsq[fi]);
-                        rsq[fi] = fmaf(r2, r2, rsq[fi]);
-                        rsq[fi] = fmaf(r3, r3, rsq[fi]);
-                    }
-                } else {
-                    *reinterpret_cast<uint2*>(out + d.a_off + (int64_t)i * d.m_pad + jb) = ow;
+                if (MODE == NS_UPDATE && ROWSTATS) {
+                    const float r0 = bf16_lo(ow.x), r1 = bf16_hi(ow.x), r2 = bf16_lo(ow.y), r3 = bf16_hi(ow.y);
+                    rsq[fi] = fmaf(r0, r0, rsq[fi]);
+                    rsq[fi] = fmaf(r1, r1, rsq[fi]);
+                    rsq[fi] = fmaf(r2, r2, rsq[fi]);
+                    rsq[fi] = fmaf(r3, r3, rsq[fi]);
                 }
             }
         }
     }
+    if (MODE == NS_POLY) __syncthreads();  // the staged A tile is read; LDS is reused below
+#pragma unroll
+    for (int fi = 0; fi < FR; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < FR; ++fj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                lds64((wi * WT + fi * 32 + l32) * EROW + 2 * (wj * WT + fj * 32 + 8 * g + 4 * hi)) = ev[fi][fj][g];
+    __syncthreads();
+
+    // the tile itself: each thread moves 16-byte row chunks, a wave covers whole rows
+    {
+        bf16* obase = MODE == NS_UPDATE ? out + d.x_off + (int64_t)i0 * d.n_pad + j0
+                                        : out + d.a_off + (int64_t)i0 * d.m_pad + j0;
+        const int ld = MODE == NS_UPDATE ? d.n_pad : d.m_pad;
+        constexpr int CPR = T / 8;
+#pragma unroll
+        for (int q = 0; q < T * CPR / kThreads; ++q) {
+            const int id = tid + kThreads * q;
+            const int r = id / CPR, c = id % CPR;
+            const uint2 lo = lds64(r * EROW + 16 * c);
+            const uint2 up = lds64(r * EROW + 16 * c + 8);
+            *reinterpret_cast<uint4*>(obase + (int64_t)r * ld + 8 * c) = make_uint4(lo.x, lo.y, up.x, up.y);
+        }
+    }
     if (MODE != NS_UPDATE && w.ti != w.tj) {
-        // mirror tile: the transposed entries, 2 bytes each; for fixed (fj, g, e)
-        // the 32 lanes of a half-wave write 64 contiguous bytes of one row
-        uint16_t* om = reinterpret_cast<uint16_t*>(out + d.a_off);
-#pragma unroll
-        for (int fi = 0; fi < FR; ++fi) {
-            const int i = i0 + wi * WT + fi * 32 + l32;
-#pragma unroll
-            for (int fj = 0; fj < FR; ++fj)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int jb = j0 + wj * WT + fj * 32 + 8 * g + 4 * hi;
-                    const uint2 ow = ev[fi][fj][g];
-                    om[(int64_t)(jb + 0) * d.m_pad + i] = (uint16_t)(ow.x & 0xffffu);
-                    om[(int64_t)(jb + 1) * d.m_pad + i] = (uint16_t)(ow.x >> 16);
-                    om[(int64_t)(jb + 2) * d.m_pad + i] = (uint16_t)(ow.y & 0xffffu);
-                    om[(int64_t)(jb + 3) * d.m_pad + i] = (uint16_t)(ow.y >> 16);
-                }
+        // the mirror tile, read column-wise with ds_read_b64_tr_b16: in each
+        // 16-lane group G, lane s = 4e + q points at row IB + 16G + 4q + e of
+        // column chunk JB, so lane 4q + c receives rows IB + 16G + 4q .. +3 of
+        // column JB + c; the 16 lanes with the same c then hold 64 consecutive
+        // entries (one 128-byte line) of mirror row JB + c.
+        bf16* mbase = out + d.a_off + (int64_t)j0 * d.m_pad + i0;
+        const int G = lane >> 4, sl = lane & 15;
+        const int sup_row = 16 * G + 4 * (sl & 3) + (sl >> 2);
+        const int rc = sl & 3, rq = sl >> 2;
+        constexpr int NIT = (T / 4) * (T / 64) / 4;  // instructions per wave
+#pragma unroll 4
+        for (int k = 0; k < NIT; ++k) {
+            const int it = wave + 4 * k;
+            const int JB = 4 * (it % (T / 4));
+            const int IB = 64 * (it / (T / 4));
+            const bf16x4 v = tr_read(smem + (IB + sup_row) * EROW + 2 * JB);
+            *reinterpret_cast<bf16x4*>(mbase + (int64_t)(JB + rc) * d.m_pad + IB + 16 * G + 4 * rq) = v;
         }
     }
 
     if (MODE == NS_UPDATE && ROWSTATS) {
+        __syncthreads();  // the staged output tile has been read
         float* rl = reinterpret_cast<float*>(smem);  // [2 wi][2 wj][WT]
 #pragma unroll
         for (int f = 0; f < FR; ++f) rsq[f] += __shfl_xor(rsq[f], 32, 64);
