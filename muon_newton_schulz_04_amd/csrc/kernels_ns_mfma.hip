@@ -66,22 +66,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int T, int MODE, bool ROWSTATS>
-__global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__ mats,
+template <int T, int WN, int MODE, bool ROWSTATS>
+__global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__ mats,
                                                      const TileWork* __restrict__ work, const bf16* __restrict__ xin,
                                                      const bf16* __restrict__ ain, bf16* __restrict__ out, float ca,
                                                      float cb, float cc, int first, const float* __restrict__ partials,
                                                      float* __restrict__ ss_arr, float* __restrict__ scale_arr,
                                                      int32_t* __restrict__ status_arr, float eps,
                                                      float* __restrict__ rowpart) {
-    constexpr int WT = T / 2;
-    constexpr int FR = WT / 32;
+    // 2 x WN waves; each wave owns a WTM x WTN block of the tile
+    constexpr int NT = 128 * WN;                     // threads per workgroup
+    constexpr int NWV = NT / 64;                     // waves
+    constexpr int WTM = T / 2;
+    constexpr int WTN = T / WN;
+    constexpr int FRI = WTM / 32;
+    constexpr int FRJ = WTN / 32;
     using LY = Layout<T>;
-    constexpr int NCH = T * BK * 2 / 16 / kThreads;  // 16-byte chunks per thread per operand
-    static_assert(NCH >= 1, "tile too small");
+    constexpr int NCH = T * BK * 2 / 16 / NT;        // 16-byte chunks per thread per operand
+    constexpr int PSTEP = NT / 8;                    // rows between a thread's P chunks
+    constexpr int XSTEP = NT / (T / 8);              // X rows between a thread's chunks
+    static_assert(NCH >= 1 && FRJ >= 1, "tile too small for this wave grid");
 
     __shared__ __attribute__((aligned(16))) char smem[2 * LY::STAGE];
-    __shared__ float red[4];
+    __shared__ float red[NWV];
 
     const TileWork w = work[blockIdx.x];
     const MatDesc d = mats[w.mat];
@@ -90,8 +97,8 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wi = wave >> 1;
-    const int wj = wave & 1;
+    const int wi = wave / WN;
+    const int wj = wave % WN;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
@@ -134,15 +141,15 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
     auto load_stage = [&](int k0, int which) {
         if (which & 1) {
 #pragma unroll
-            for (int q = 0; q < NCH; ++q) preg[q] = bload(rp, vp, (q * 32 * ldp + k0) * 2);
+            for (int q = 0; q < NCH; ++q) preg[q] = bload(rp, vp, (q * PSTEP * ldp + k0) * 2);
         }
         if (which & 2) {
 #pragma unroll
             for (int q = 0; q < NCH; ++q) {
                 if (MODE != NS_UPDATE)
-                    qreg[q] = bload(rq, vq, (q * 32 * ldq + k0) * 2);
+                    qreg[q] = bload(rq, vq, (q * PSTEP * ldq + k0) * 2);
                 else
-                    qreg[q] = bload(rq, vq, (q * (kThreads / (T / 8)) + k0) * ldq * 2);
+                    qreg[q] = bload(rq, vq, (q * XSTEP + k0) * ldq * 2);
             }
         }
     };
@@ -151,39 +158,41 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
         char* P = smem + s * LY::STAGE;
         char* Q = P + LY::KTILE;
 #pragma unroll
-        for (int q = 0; q < NCH; ++q) *reinterpret_cast<uint4*>(P + sp + q * 32 * KROW) = preg[q];
+        for (int q = 0; q < NCH; ++q) *reinterpret_cast<uint4*>(P + sp + q * PSTEP * KROW) = preg[q];
 #pragma unroll
         for (int q = 0; q < NCH; ++q) {
             if (MODE != NS_UPDATE)
-                *reinterpret_cast<uint4*>(Q + sq + q * 32 * KROW) = qreg[q];
+                *reinterpret_cast<uint4*>(Q + sq + q * PSTEP * KROW) = qreg[q];
             else
-                *reinterpret_cast<uint4*>(Q + sq + q * (kThreads / (T / 8)) * LY::XROW) = qreg[q];
+                *reinterpret_cast<uint4*>(Q + sq + q * XSTEP * LY::XROW) = qreg[q];
         }
     };
 
-    f32x16 acc[FR][FR];
+    f32x16 acc[FRI][FRJ];
 #pragma unroll
-    for (int a = 0; a < FR; ++a)
+    for (int a = 0; a < FRI; ++a)
 #pragma unroll
-        for (int b = 0; b < FR; ++b)
+        for (int b = 0; b < FRJ; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
     // lane bases of the fragment reads
-    const int fp = (wi * WT + l32) * KROW + 16 * hi;          // + f 32 KROW + 32 ks
-    const int fq = (wj * WT + l32) * KROW + 16 * hi;
+    const int fp = (wi * WTM + l32) * KROW + 16 * hi;         // + f 32 KROW + 32 ks
+    const int fq = (wj * WTN + l32) * KROW + 16 * hi;
     const int g16 = lane >> 4;
     const int s16 = lane & 15;
-    const int ft = (8 * (g16 >> 1) + (s16 >> 2)) * LY::XROW + 2 * (wj * WT + 16 * (g16 & 1) + 4 * (s16 & 3));
+    const int ft = (8 * (g16 >> 1) + (s16 >> 2)) * LY::XROW + 2 * (wj * WTN + 16 * (g16 & 1) + 4 * (s16 & 3));
     // + (16 ks + 4 h) XROW + 64 f
 
     // two fragment sets, alternating between k16 sub-steps
-    bf16x8 pfr[2][FR], qfr[2][FR];
+    bf16x8 pfr[2][FRI], qfr[2][FRJ];
     auto read_frags = [&](const char* P, int ks, int set) {
         const char* Q = P + LY::KTILE;
 #pragma unroll
-        for (int f = 0; f < FR; ++f) {
+        for (int f = 0; f < FRI; ++f)
             pfr[set][f] = *reinterpret_cast<const bf16x8*>(P + fp + f * 32 * KROW + 32 * ks);
+#pragma unroll
+        for (int f = 0; f < FRJ; ++f) {
             if (MODE != NS_UPDATE) {
                 qfr[set][f] = *reinterpret_cast<const bf16x8*>(Q + fq + f * 32 * KROW + 32 * ks);
             } else {
@@ -193,43 +202,67 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
             }
         }
     };
-    constexpr int NREAD = MODE == NS_UPDATE ? 3 * FR : 2 * FR;  // LDS read instructions per sub-step
+    constexpr int NREAD = FRI + (MODE == NS_UPDATE ? 2 : 1) * FRJ;  // LDS read instructions per sub-step
 
     // One K stage. MORE: a next stage exists (its loads and LDS writes are
     // interleaved here); the last stage is peeled so the steady-state loop
     // body has no branches for the scheduler to stop at.
+    auto mfma_block = [&](int set, int lo, int hi_) {
+#pragma unroll
+        for (int f = lo; f < hi_; ++f) {
+            const int fi = f / FRJ, fj = f % FRJ;
+            acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[set][fj], pfr[set][fi], acc[fi][fj], 0, 0, 0);
+        }
+    };
     auto stage = [&](int kt, auto more_c) {
         constexpr bool MORE = decltype(more_c)::value;
+        constexpr int NW = 2 * NCH;
+        constexpr int NF = FRI * FRJ;
         const char* P = smem + (kt & 1) * LY::STAGE;
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
+        for (int ks = 0; ks < BK / 16 - 1; ++ks) {
             const int set = ks & 1;
-            if (ks + 1 < BK / 16) read_frags(P, ks + 1, set ^ 1);
+            read_frags(P, ks + 1, set ^ 1);
             // the next stage's global loads are spread over sub-steps 0 and 1
-            // (one per MFMA) and land in the other LDS buffer in sub-step 3
             if constexpr (MORE) {
                 if (ks == 0) load_stage((kt + 1) * BK, 1);
                 if (ks == 1) load_stage((kt + 1) * BK, 2);
-                if (ks == 3) store_stage((kt & 1) ^ 1);
             }
+            mfma_block(set, 0, NF);
+            // interleave: one MFMA, then one LDS read / global load
 #pragma unroll
-            for (int fi = 0; fi < FR; ++fi)
-#pragma unroll
-                for (int fj = 0; fj < FR; ++fj)
-                    acc[fi][fj] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[set][fj], pfr[set][fi], acc[fi][fj], 0, 0, 0);
-            // interleave: one MFMA, then one LDS read / global load / LDS write
-            constexpr int NW = 2 * NCH;
-#pragma unroll
-            for (int i = 0; i < FR * FR; ++i) {
+            for (int i = 0; i < NF; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (ks + 1 < BK / 16 && i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 if (MORE && ks < 2 && i < NCH) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                if (MORE && ks == 3 && i < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
         }
-        __syncthreads();
-        if constexpr (MORE) read_frags(smem + ((kt + 1) & 1) * LY::STAGE, 0, 0);
+        // last sub-step: half its MFMAs carry the next stage's LDS writes; the
+        // barrier comes next, and the next stage's first fragment reads run
+        // under the other half
+        constexpr int SL = (BK / 16 - 1) & 1;
+        if constexpr (MORE) {
+            store_stage((kt & 1) ^ 1);
+            mfma_block(SL, 0, NF / 2);
+#pragma unroll
+            for (int i = 0; i < NF / 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            }
+            if (NW > NF / 2) __builtin_amdgcn_sched_group_barrier(0x200, NW - NF / 2, 0);
+            __syncthreads();
+            read_frags(smem + ((kt + 1) & 1) * LY::STAGE, 0, 0);
+            mfma_block(SL, NF / 2, NF);
+#pragma unroll
+            for (int i = 0; i < NF / 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if (NREAD > NF / 2) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NF / 2, 0);
+        } else {
+            mfma_block(SL, 0, NF);
+            __syncthreads();
+        }
     };
 
     const int nk = K / BK;
@@ -244,8 +277,13 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
     float alpha = 1.0f;
     if (MODE == NS_GRAM && first) {
         float acc_p = 0.f;
-        for (int p = tid; p < d.ew_count; p += kThreads) acc_p += partials[d.ew_start + p];
-        const float total = block_sum_256(acc_p, red);
+        for (int p = tid; p < d.ew_count; p += NT) acc_p += partials[d.ew_start + p];
+        acc_p = wave_sum(acc_p);
+        if (lane == 0) red[wave] = acc_p;
+        __syncthreads();
+        float total = 0.f;
+#pragma unroll
+        for (int v = 0; v < NWV; ++v) total += red[v];
         const float sc = 1.0f / (sqrtf(total) + eps);
         alpha = sc * sc;
         if (w.ti == 0 && w.tj == 0 && tid == 0) {
@@ -267,9 +305,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
         const bf16* Asrc = ain + d.a_off + (int64_t)i0 * d.m_pad + j0;
         const __amdgpu_buffer_rsrc_t ra = rsrc(Asrc, (uint32_t)(T * d.m_pad * 2));
         constexpr int CPR = T / 8;                   // 16-byte chunks per row
-        constexpr int NE = T * CPR / kThreads;       // chunks per thread
+        constexpr int NE = T * CPR / NT;             // chunks per thread
         const int er = tid / CPR, ec = tid % CPR;
-        constexpr int RSTEP = kThreads / CPR;
+        constexpr int RSTEP = NT / CPR;
 #pragma unroll
         for (int b0 = 0; b0 < NE; b0 += NCH) {
 #pragma unroll
@@ -285,19 +323,19 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
         __syncthreads();
     }
 
-    float rsq[FR];
+    float rsq[FRI];
 #pragma unroll
-    for (int f = 0; f < FR; ++f) rsq[f] = 0.f;
+    for (int f = 0; f < FRI; ++f) rsq[f] = 0.f;
 
-    uint2 ev[FR][FR][4];
+    uint2 ev[FRI][FRJ][4];
 #pragma unroll
-    for (int fi = 0; fi < FR; ++fi) {
-        const int il = wi * WT + fi * 32 + l32;
+    for (int fi = 0; fi < FRI; ++fi) {
+        const int il = wi * WTM + fi * 32 + l32;
 #pragma unroll
-        for (int fj = 0; fj < FR; ++fj) {
+        for (int fj = 0; fj < FRJ; ++fj) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int jl = wj * WT + fj * 32 + 8 * g + 4 * hi;
+                const int jl = wj * WTN + fj * 32 + 8 * g + 4 * hi;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[fi][fj][4 * g + e];
@@ -333,12 +371,12 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
     }
     if (MODE == NS_POLY) __syncthreads();  // the staged A tile is read; LDS is reused below
 #pragma unroll
-    for (int fi = 0; fi < FR; ++fi)
+    for (int fi = 0; fi < FRI; ++fi)
 #pragma unroll
-        for (int fj = 0; fj < FR; ++fj)
+        for (int fj = 0; fj < FRJ; ++fj)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                lds64((wi * WT + fi * 32 + l32) * EROW + 2 * (wj * WT + fj * 32 + 8 * g + 4 * hi)) = ev[fi][fj][g];
+                lds64((wi * WTM + fi * 32 + l32) * EROW + 2 * (wj * WTN + fj * 32 + 8 * g + 4 * hi)) = ev[fi][fj][g];
     __syncthreads();
 
     // the tile itself: each thread moves 16-byte row chunks, a wave covers whole rows
@@ -348,8 +386,8 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
         const int ld = MODE == NS_UPDATE ? d.n_pad : d.m_pad;
         constexpr int CPR = T / 8;
 #pragma unroll
-        for (int q = 0; q < T * CPR / kThreads; ++q) {
-            const int id = tid + kThreads * q;
+        for (int q = 0; q < T * CPR / NT; ++q) {
+            const int id = tid + NT * q;
             const int r = id / CPR, c = id % CPR;
             const uint2 lo = lds64(r * EROW + 16 * c);
             const uint2 up = lds64(r * EROW + 16 * c + 8);
@@ -366,10 +404,10 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
         const int G = lane >> 4, sl = lane & 15;
         const int sup_row = 16 * G + 4 * (sl & 3) + (sl >> 2);
         const int rc = sl & 3, rq = sl >> 2;
-        constexpr int NIT = (T / 4) * (T / 64) / 4;  // instructions per wave
+        constexpr int NIT = (T / 4) * (T / 64) / NWV;  // instructions per wave
 #pragma unroll 4
         for (int k = 0; k < NIT; ++k) {
-            const int it = wave + 4 * k;
+            const int it = wave + NWV * k;
             const int JB = 4 * (it % (T / 4));
             const int IB = 64 * (it / (T / 4));
             const bf16x4 v = tr_read(smem + (IB + sup_row) * EROW + 2 * JB);
@@ -379,24 +417,26 @@ __global__ __launch_bounds__(kThreads) void k_ns_big(const MatDesc* __restrict__
 
     if (MODE == NS_UPDATE && ROWSTATS) {
         __syncthreads();  // the staged output tile has been read
-        float* rl = reinterpret_cast<float*>(smem);  // [2 wi][2 wj][WT]
+        float* rl = reinterpret_cast<float*>(smem);  // [2 wi][WN wj][WTM]
 #pragma unroll
-        for (int f = 0; f < FR; ++f) rsq[f] += __shfl_xor(rsq[f], 32, 64);
+        for (int f = 0; f < FRI; ++f) rsq[f] += __shfl_xor(rsq[f], 32, 64);
         if (hi == 0) {
 #pragma unroll
-            for (int f = 0; f < FR; ++f) rl[(wi * 2 + wj) * WT + f * 32 + l32] = rsq[f];
+            for (int f = 0; f < FRI; ++f) rl[(wi * WN + wj) * WTM + f * 32 + l32] = rsq[f];
         }
         __syncthreads();
         if (tid < T) {
-            const int wr = tid / WT;
-            const int rr = tid % WT;
-            const float sum = rl[(wr * 2 + 0) * WT + rr] + rl[(wr * 2 + 1) * WT + rr];
+            const int wr = tid / WTM;
+            const int rr = tid % WTM;
+            float sum = 0.f;
+#pragma unroll
+            for (int v = 0; v < WN; ++v) sum += rl[(wr * WN + v) * WTM + rr];
             rowpart[d.rowpart_off + (int64_t)w.tj * d.m_pad + i0 + tid] = sum;
         }
     }
 }
 
-template <int T>
+template <int T, int WN>
 hipError_t launch_big_T(const LaunchCtx& L, const GemmList& G, int mode, const void* xin, const void* ain, void* out,
                         float ca, float cb, float cc, int first, float eps, int rowstats) {
     const TileWork* wl = mode == NS_GRAM ? G.gram : mode == NS_POLY ? G.poly : G.update;
@@ -405,19 +445,20 @@ hipError_t launch_big_T(const LaunchCtx& L, const GemmList& G, int mode, const v
     const bf16* x = (const bf16*)xin;
     const bf16* a = (const bf16*)ain;
     bf16* o = (bf16*)out;
+    constexpr int NT = 128 * WN;
     if (mode == NS_GRAM)
-        k_ns_big<T, NS_GRAM, false><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials,
-                                                                  L.ss, L.scale, L.status, eps, L.rowpart);
+        k_ns_big<T, WN, NS_GRAM, false><<<n, NT, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials,
+                                                                L.ss, L.scale, L.status, eps, L.rowpart);
     else if (mode == NS_POLY)
-        k_ns_big<T, NS_POLY, false><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials,
-                                                                  L.ss, L.scale, L.status, eps, L.rowpart);
+        k_ns_big<T, WN, NS_POLY, false><<<n, NT, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials,
+                                                                L.ss, L.scale, L.status, eps, L.rowpart);
     else if (rowstats)
-        k_ns_big<T, NS_UPDATE, true><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first,
-                                                                   L.partials, L.ss, L.scale, L.status, eps, L.rowpart);
+        k_ns_big<T, WN, NS_UPDATE, true><<<n, NT, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first,
+                                                                 L.partials, L.ss, L.scale, L.status, eps, L.rowpart);
     else
-        k_ns_big<T, NS_UPDATE, false><<<n, kThreads, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first,
-                                                                    L.partials, L.ss, L.scale, L.status, eps,
-                                                                    L.rowpart);
+        k_ns_big<T, WN, NS_UPDATE, false><<<n, NT, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first,
+                                                                  L.partials, L.ss, L.scale, L.status, eps,
+                                                                  L.rowpart);
     return hipGetLastError();
 }
 
@@ -425,8 +466,8 @@ hipError_t launch_big_T(const LaunchCtx& L, const GemmList& G, int mode, const v
 
 hipError_t launch_ns_stage_big(const LaunchCtx& L, const GemmList& G, int mode, const void* xin, const void* ain,
                                void* out, float ca, float cb, float cc, int first, float eps, int rowstats) {
-    if (G.T == 256) return launch_big_T<256>(L, G, mode, xin, ain, out, ca, cb, cc, first, eps, rowstats);
-    return launch_big_T<128>(L, G, mode, xin, ain, out, ca, cb, cc, first, eps, rowstats);
+    if (G.T == 256) return launch_big_T<256, 4>(L, G, mode, xin, ain, out, ca, cb, cc, first, eps, rowstats);
+    return launch_big_T<128, 2>(L, G, mode, xin, ain, out, ca, cb, cc, first, eps, rowstats);
 }
 
 }  // namespace muon
