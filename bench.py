@@ -33,16 +33,17 @@ GRAD_POOL = 4               # distinct gradient sets cycled through the timed st
 
 def _kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("kernels_ns.hip", "kernels_ns_mfma.hip", "kernels_elementwise.hip", "kernel_common.hpp"):
+    for f in ("kernels_ns.hip", "kernels_ns_mfma.hip", "kernels_elementwise.hip", "kernel_common.hpp",
+              "device_types.hpp", "plan.cpp", "api.cpp"):
         with open(os.path.join(ROOT, "muon_newton_schulz_04_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel: str, workload: str, launches_bytes: float):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+def _traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -50,9 +51,84 @@ def _traffic(kernel: str, workload: str, launches_bytes: float):
             t = json.load(f)
         if t.get("source_hash") != _kernel_source_hash():
             return None
-        return float(t["hbm_bytes_per_launch"])
+        return float(t["kernels"][kernel]["hbm_bytes_per_launch"])
     except Exception:
         return None
+
+
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
+
+
+def copy_calibration() -> None:
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) measured on the same box."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    # torch's elementwise negation: one streaming read and one streaming write
+    # of 1 GiB each (a same-dtype copy_ would go to the DMA engines instead).
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _pmc_rows(d: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    with open(files[0]) as f:
+        yield from csv.DictReader(f)
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str) -> dict:
+    """Per-launch HBM traffic of each NS kernel class from two rocprofv3
+    --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by
+    what the same counter reads for the 1 GiB calibration copy."""
+    import statistics
+    per = {}
+    unmatched = set()
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = {}
+        for r in _pmc_rows(d):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            if "neg_kernel" in name:
+                key = "copy"
+            elif "k_ns_big<" in name or "k_ns<" in name:
+                mode = name.split("<", 1)[1].split(">", 1)[0].split(",")
+                key = {"0": "gram", "1": "poly", "2": "update"}[mode[-2].strip() if "big" in name else mode[2].strip()]
+            elif "k_momentum" in name:
+                key = "momentum"
+            elif "k_apply" in name:
+                key = "apply"
+            else:
+                unmatched.add(name[:80])
+                continue
+            vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        per[counter] = {k: statistics.median(v) for k, v in vals.items()}
+    fscale = COPY_BYTES / per["FETCH_SIZE"]["copy"]
+    wscale = COPY_BYTES / per["WRITE_SIZE"]["copy"]
+    cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc {c} -f csv -d $REPO/gpurun_out/{d} "
+           "-o run -- python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-events --copy-calibration")
+    out = {"workload": workload, "source_hash": _kernel_source_hash(),
+           "commands": [cmd.format(c="FETCH_SIZE", d="pmc_fetch"), cmd.format(c="WRITE_SIZE", d="pmc_write"),
+                        "python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write"],
+           "note": "FETCH_SIZE/WRITE_SIZE are KiB per dispatch; each is scaled so that the 1 GiB calibration "
+                   "read/write (torch.neg over 2^28 floats) counts 2^30 bytes; medians over dispatches",
+           "copy_fetch_bytes": per["FETCH_SIZE"]["copy"], "copy_write_bytes": per["WRITE_SIZE"]["copy"],
+           "fetch_scale": fscale, "write_scale": wscale, "kernels": {}}
+    for k in per["FETCH_SIZE"]:
+        if k == "copy" or k not in per["WRITE_SIZE"]:
+            continue
+        out["kernels"][k] = {"fetch_bytes": per["FETCH_SIZE"][k] * fscale,
+                             "write_bytes": per["WRITE_SIZE"][k] * wscale,
+                             "hbm_bytes_per_launch": per["FETCH_SIZE"][k] * fscale + per["WRITE_SIZE"][k] * wscale}
+    if unmatched:
+        print("unmatched kernels:", sorted(unmatched), file=sys.stderr)
+    return out
 
 
 def cpu_baseline(seconds: float) -> dict:
@@ -103,7 +179,22 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="do not time kernels with events")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 1 GiB once per pass (HBM counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into "
+                         "profiles/traffic_<workload>.json and exit")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        from workloads import get_workload as _gw
+        wname = _gw(args.config).name
+        t = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wname)
+        path = os.path.join(ROOT, "profiles", f"traffic_{wname}.json")
+        with open(path, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t, indent=1))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the sharded "
@@ -191,7 +282,7 @@ def main() -> int:
                         "frac": achieved / PEAK_HBM_GBS, "kernel": dom,
                         "alg_per_launch": work.bytes[kidx] / work.launches[kidx]}
         roofline["avg_launch_ms"] = e["avg_ms"]
-        roofline["traffic"] = _traffic(dom, w.name, roofline["alg_per_launch"])
+        roofline["traffic"] = _traffic(dom, w.name)
 
     out = {
         "metric": METRIC,
@@ -218,6 +309,8 @@ def main() -> int:
         "device": torch.cuda.get_device_name(0),
         "source_hash": _kernel_source_hash(),
     }
+    if args.copy_calibration:
+        copy_calibration()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
