@@ -2,30 +2,34 @@
 //
 // Same three stages as kernels_ns.hip (Gram with mirrored upper tiles,
 // polynomial epilogue, update), re-tiled for MI355X:
-//  * T x T output per 256-thread workgroup, 2 x 2 waves, each wave T/2 x T/2
-//    as (T/64)^2 blocks of v_mfma_f32_32x32x16_bf16 (T = 256: 128 x 128 per
-//    wave, 256 fp32 accumulators per lane), which halves LDS read traffic per
-//    MFMA against 64 x 64 wave tiles.
-//  * K staged in slices of 64 (128 bytes per row) through two LDS buffers;
-//    the next slice is fetched into registers while the current one feeds
-//    the MFMAs: its global loads are interleaved one per MFMA over the first
-//    two k16 sub-steps and written to LDS in the last, and the fragment reads
-//    of sub-step k+1 run under the MFMAs of sub-step k.
-//  * Operands whose contraction index is contiguous (rows of X for the
-//    Gram, rows of A, rows of B) sit in LDS as 128-byte rows padded to 144
-//    bytes, so 16 consecutive rows start in 16 distinct 16-byte bank slots.
-//  * The update contracts X over its row index. X stays row-major in LDS
-//    (rows padded to 2T + 64 bytes) and its fragments are read with
-//    ds_read_b64_tr_b16, which hands each lane four consecutive rows of one
-//    column: within a 16-lane group, lane s supplies the address of row
+//  * T x T output per workgroup of 2 x WN waves (T = 256: 8 waves, 2 per
+//    SIMD, each 128 x 64 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16).
+//  * K is staged in slices of 64 through two LDS buffers that are filled
+//    by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): a slice's
+//    loads are issued right after the barrier that frees its buffer, a whole
+//    slice ahead of its use, and no VGPRs or ds_write instructions carry them.
+//    Each load instruction lands 64 x 16 bytes contiguously in LDS, so the
+//    tiles are unpadded and bank conflicts are avoided by swizzling 16-byte
+//    chunks on the global side:
+//      - operands whose contraction index is contiguous (rows of X for the
+//        Gram, rows of A, rows of B) sit as 128-byte rows; chunk c of row r
+//        is stored at chunk c ^ ((r >> 1) & 7), so the 16 rows a 16-lane
+//        phase of ds_read_b128 touches fall in 16 distinct 16-byte slots;
+//      - the update's X tile (contraction over its rows) sits row-major as
+//        2T-byte rows; chunk c of row r is stored at c ^ (4 (r & 3)), so the
+//        4 rows x 64 bytes a half-wave of ds_read_b64_tr_b16 touches fall in
+//        4 distinct 64-byte bank windows.
+//  * ds_read_b64_tr_b16 hands each lane four consecutive rows of one column
+//    of X: within a 16-lane group, lane s supplies the address of row
 //    (s >> 2), columns 4 (s & 3) .. +3 of a 4 x 16 block, and lane i receives
 //    column i of that block. Two such reads make one 8-element fragment.
+//  * The fragment reads of sub-step k+1 run under the MFMAs of sub-step k.
+//  * On diagonal Gram / polynomial tiles both operands are the same rows,
+//    which are loaded once.
 //  * The a X term of the update is folded into the polynomial: the poly
 //    kernel writes B' = a I + b A + c A A, so the update is the pure product
-//    X' = alpha B' X and reads X once per iteration.
-//  * Every LDS address is a lane base plus a compile-time offset and every
-//    global load is a buffer load with a lane offset and a scalar offset, so
-//    the 256 accumulators leave room for the staged next slice in registers.
+//    X' = alpha B' X and reads X once per iteration. The poly kernel's own
+//    A tile (for the b A term) streams into LDS during its last K slice.
 //
 // Source of the iteration: [P4] "modded-nanogpt 50B-token 长时程训练实验解析",
 // section "从源码看 Muon 的分布式正交化实现" (quintic Newton–Schulz in bf16).
@@ -43,15 +47,14 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int BK = 64;       // k per LDS stage
-constexpr int KROW = 144;    // bytes per padded row of a k-contiguous tile (128 + 16)
+constexpr int KROWB = 128;   // bytes per row of a k-contiguous tile (BK bf16, swizzled)
 
 template <int T>
 struct Layout {
-    static constexpr int XROW = 2 * T + 64;            // bytes per padded row of the X tile
-    static constexpr int KTILE = T * KROW;              // k-contiguous tile, one stage
-    static constexpr int XTILE = BK * XROW;             // X tile, one stage
-    static constexpr int QTILE = KTILE > XTILE ? KTILE : XTILE;
-    static constexpr int STAGE = KTILE + QTILE;
+    static constexpr int XROWB = 2 * T;                 // bytes per row of the X tile (swizzled)
+    static constexpr int KTILE = T * KROWB;             // k-contiguous tile, one stage
+    static constexpr int STAGE = 2 * KTILE;             // P tile + (k-contiguous Q or X) tile
+    static_assert(BK * XROWB == KTILE, "X tile and k-contiguous tile have the same size");
 };
 
 __device__ __forceinline__ bf16x4 tr_read(const char* p) {
@@ -62,9 +65,17 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int voff, int s
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// 16 bytes per lane, global -> LDS: lane i lands at lds + 16 i (lds is wave-uniform)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(LDS_AS char*)lds, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+// s_waitcnt vmcnt(0), leaving the LDS / scalar counters alone
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int T, int WN, int MODE, bool ROWSTATS>
 __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__ mats,
@@ -82,12 +93,11 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     constexpr int FRI = WTM / 32;
     constexpr int FRJ = WTN / 32;
     using LY = Layout<T>;
-    constexpr int NCH = T * BK * 2 / 16 / NT;        // 16-byte chunks per thread per operand
-    constexpr int PSTEP = NT / 8;                    // rows between a thread's P chunks
-    constexpr int XSTEP = NT / (T / 8);              // X rows between a thread's chunks
-    static_assert(NCH >= 1 && FRJ >= 1, "tile too small for this wave grid");
+    constexpr int EROW = 2 * T + 8;                  // epilogue staging row (bytes)
+    constexpr int SMEM = 2 * LY::STAGE > T * EROW ? 2 * LY::STAGE : T * EROW;
+    static_assert(FRJ >= 1 && NWV % 2 == 0, "tile too small for this wave grid");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * LY::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
     __shared__ float red[NWV];
 
     const TileWork w = work[blockIdx.x];
@@ -96,11 +106,13 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     const int j0 = (int)w.tj * T;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wi = wave / WN;
     const int wj = wave % WN;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
+    // diagonal Gram / polynomial tile: both operands are the same rows
+    const bool same = MODE != NS_UPDATE && w.ti == w.tj;
 
     const bf16* Psrc;
     const bf16* Qsrc;
@@ -126,45 +138,40 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     const __amdgpu_buffer_rsrc_t rp = rsrc(Psrc, (uint32_t)(T * ldp * 2));
     const __amdgpu_buffer_rsrc_t rq =
         rsrc(Qsrc, (uint32_t)((MODE == NS_UPDATE ? K * ldq : T * ldq) * 2));
-    // lane parts of the global offsets (bytes)
-    const int vp = (tid >> 3) * ldp * 2 + (tid & 7) * 16;
-    const int vq = MODE == NS_UPDATE ? (tid / (T / 8)) * ldq * 2 + (tid % (T / 8)) * 16
-                                     : (tid >> 3) * ldq * 2 + (tid & 7) * 16;
-    // lane parts of the LDS store offsets
-    const int sp = (tid >> 3) * KROW + (tid & 7) * 16;
-    const int sq = MODE == NS_UPDATE ? (tid / (T / 8)) * LY::XROW + (tid % (T / 8)) * 16 : sp;
 
-    uint4 preg[NCH];
-    uint4 qreg[NCH];
+    // ---- direct-to-LDS load geometry ----
+    // k-contiguous tile: instruction q of wave w fills rows q KROUND + 8 w .. +7;
+    // lane l takes physical chunk l & 7 of row 8 w + (l >> 3), i.e. logical chunk
+    // (l & 7) ^ ((row >> 1) & 7) (q KROUND is a multiple of 16: same swizzle)
+    constexpr int KROUND = 8 * NWV;
+    constexpr int NKI = T / KROUND;
+    const int kr = wave * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ ((kr >> 1) & 7);
+    const int vp = kr * ldp * 2 + kc * 16;
+    const int vqk = kr * ldq * 2 + kc * 16;
+    // X tile (update): XRPI rows of XCH chunks per instruction; lane l takes
+    // physical chunk l % XCH of row w XRPI + l / XCH, logical chunk ^ 4 (row & 3)
+    constexpr int XCH = T / 8;
+    constexpr int XRPI = 64 / XCH;
+    constexpr int XROUND = XRPI * NWV;
+    constexpr int NXI = BK / XROUND;
+    static_assert(NKI >= 1 && NXI >= 1 && XROUND % 4 == 0, "load geometry");
+    const int xr = wave * XRPI + lane / XCH;
+    const int xc = (lane % XCH) ^ (4 * (xr & 3));
+    const int vqx = xr * ldq * 2 + xc * 16;
 
-    // global -> registers for one stage; which = 1: P chunks, 2: Q chunks, 3: both
-    auto load_stage = [&](int k0, int which) {
-        if (which & 1) {
+    auto dma_stage = [&](int kt, char* S) {
+        const int k0 = kt * BK;
 #pragma unroll
-            for (int q = 0; q < NCH; ++q) preg[q] = bload(rp, vp, (q * PSTEP * ldp + k0) * 2);
-        }
-        if (which & 2) {
+        for (int q = 0; q < NKI; ++q) dma16(rp, S + (q * KROUND + wave * 8) * KROWB, vp, (q * KROUND * ldp + k0) * 2);
+        if (MODE == NS_UPDATE) {
 #pragma unroll
-            for (int q = 0; q < NCH; ++q) {
-                if (MODE != NS_UPDATE)
-                    qreg[q] = bload(rq, vq, (q * PSTEP * ldq + k0) * 2);
-                else
-                    qreg[q] = bload(rq, vq, (q * XSTEP + k0) * ldq * 2);
-            }
-        }
-    };
-
-    auto store_stage = [&](int s) {
-        char* P = smem + s * LY::STAGE;
-        char* Q = P + LY::KTILE;
+            for (int q = 0; q < NXI; ++q)
+                dma16(rq, S + LY::KTILE + (q * XROUND + wave * XRPI) * LY::XROWB, vqx, (k0 + q * XROUND) * ldq * 2);
+        } else if (!same) {
 #pragma unroll
-        for (int q = 0; q < NCH; ++q) *reinterpret_cast<uint4*>(P + sp + q * PSTEP * KROW) = preg[q];
-#pragma unroll
-        for (int q = 0; q < NCH; ++q) {
-            if (MODE != NS_UPDATE)
-                *reinterpret_cast<uint4*>(Q + sq + q * PSTEP * KROW) = qreg[q];
-            else
-                *reinterpret_cast<uint4*>(Q + sq + q * XSTEP * LY::XROW) = qreg[q];
+            for (int q = 0; q < NKI; ++q)
+                dma16(rq, S + LY::KTILE + (q * KROUND + wave * 8) * KROWB, vqk, (q * KROUND * ldq + k0) * 2);
         }
     };
 
@@ -176,37 +183,65 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    // lane bases of the fragment reads
-    const int fp = (wi * WTM + l32) * KROW + 16 * hi;         // + f 32 KROW + 32 ks
-    const int fq = (wj * WTN + l32) * KROW + 16 * hi;
+    // ---- fragment read geometry ----
+    // k-contiguous: lane reads row l32 of a 32-row block, logical chunk 2 ks + hi
+    int fo[BK / 16];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) fo[ks] = l32 * KROWB + 16 * ((2 * ks + hi) ^ ((l32 >> 1) & 7));
+    const int pb = wi * WTM * KROWB;
+    const int qb = wj * WTN * KROWB + (same ? 0 : LY::KTILE);
+    // X (update): lane s of 16-lane group g reads row 8 (g >> 1) + (s >> 2) (+ 16 ks + 4 h),
+    // elements wj WTN + 32 f + 16 (g & 1) + 4 (s & 3) .. +3
     const int g16 = lane >> 4;
     const int s16 = lane & 15;
-    const int ft = (8 * (g16 >> 1) + (s16 >> 2)) * LY::XROW + 2 * (wj * WTN + 16 * (g16 & 1) + 4 * (s16 & 3));
-    // + (16 ks + 4 h) XROW + 64 f
+    const int trow = 8 * (g16 >> 1) + (s16 >> 2);
+    int tb[FRJ];
+#pragma unroll
+    for (int f = 0; f < FRJ; ++f) {
+        const int e = wj * WTN + 32 * f + 16 * (g16 & 1) + 4 * (s16 & 3);
+        tb[f] = LY::KTILE + trow * LY::XROWB + 16 * ((e >> 3) ^ (4 * (trow & 3))) + 2 * (e & 7);
+    }
 
     // two fragment sets, alternating between k16 sub-steps
     bf16x8 pfr[2][FRI], qfr[2][FRJ];
-    auto read_frags = [&](const char* P, int ks, int set) {
-        const char* Q = P + LY::KTILE;
+    auto read_frags = [&](const char* S, int ks, int set) {
 #pragma unroll
         for (int f = 0; f < FRI; ++f)
-            pfr[set][f] = *reinterpret_cast<const bf16x8*>(P + fp + f * 32 * KROW + 32 * ks);
+            pfr[set][f] = *reinterpret_cast<const bf16x8*>(S + pb + fo[ks] + f * 32 * KROWB);
 #pragma unroll
         for (int f = 0; f < FRJ; ++f) {
             if (MODE != NS_UPDATE) {
-                qfr[set][f] = *reinterpret_cast<const bf16x8*>(Q + fq + f * 32 * KROW + 32 * ks);
+                qfr[set][f] = *reinterpret_cast<const bf16x8*>(S + qb + fo[ks] + f * 32 * KROWB);
             } else {
-                const bf16x4 lo = tr_read(Q + ft + (16 * ks) * LY::XROW + 64 * f);
-                const bf16x4 up = tr_read(Q + ft + (16 * ks + 4) * LY::XROW + 64 * f);
+                const bf16x4 lo = tr_read(S + tb[f] + (16 * ks) * LY::XROWB);
+                const bf16x4 up = tr_read(S + tb[f] + (16 * ks + 4) * LY::XROWB);
                 qfr[set][f] = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
             }
         }
     };
-    constexpr int NREAD = FRI + (MODE == NS_UPDATE ? 2 : 1) * FRJ;  // LDS read instructions per sub-step
+    // POLY: the output tile's own A block (for the b A term) comes into LDS as
+    // 2T-byte rows, 128 rows per stage buffer, chunk c of row r at c ^ (r & 15);
+    // rows [0, 128) go to the buffer the last K slice leaves free, the rest
+    // (T = 256) to the other one once that slice is done
+    constexpr int AQ = 128 / XROUND;  // load instructions per 128 rows
+    const int ar = wave * XRPI + lane / XCH;
+    const int va = ar * d.m_pad * 2 + ((lane % XCH) ^ (ar & 15)) * 16;
+    auto dma_atile = [&](int part, char* buf) {
+        if constexpr (MODE == NS_POLY) {
+            const __amdgpu_buffer_rsrc_t ra =
+                rsrc(ain + d.a_off + (int64_t)i0 * d.m_pad + j0, (uint32_t)(T * d.m_pad * 2));
+#pragma unroll
+            for (int q = 0; q < AQ; ++q) {
+                const int row = part * 128 + q * XROUND;
+                if (row < T) dma16(ra, buf + (q * XROUND + wave * XRPI) * LY::XROWB, va, row * d.m_pad * 2);
+            }
+        }
+    };
+    static_assert(MODE != NS_POLY || (T % 128 == 0 && 128 * LY::XROWB <= LY::STAGE), "A tile layout");
 
-    // One K stage. MORE: a next stage exists (its loads and LDS writes are
-    // interleaved here); the last stage is peeled so the steady-state loop
-    // body has no branches for the scheduler to stop at.
+    constexpr int NREAD = FRI + (MODE == NS_UPDATE ? 2 : 1) * FRJ;  // LDS read instructions per sub-step
+    constexpr int NDMA = NKI + (MODE == NS_UPDATE ? NXI : NKI);      // load instructions per stage
+
     auto mfma_block = [&](int set, int lo, int hi_) {
 #pragma unroll
         for (int f = lo; f < hi_; ++f) {
@@ -214,44 +249,39 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[set][fj], pfr[set][fi], acc[fi][fj], 0, 0, 0);
         }
     };
-    auto stage = [&](int kt, auto more_c) {
+    // One K stage. MORE: a next stage exists; its loads go out first (the
+    // buffer they fill was released by the barrier that ended the previous
+    // stage). The last stage is peeled so the steady-state loop body has no
+    // branches for the scheduler to stop at.
+    // S: this stage's buffer, N: the other one. Both are restrict so that the
+    // compiler knows the loads into N do not feed this stage's LDS reads and
+    // does not wait for them before each read.
+    auto stage = [&](const char* __restrict__ S, char* __restrict__ N, int kt, auto more_c) {
         constexpr bool MORE = decltype(more_c)::value;
-        constexpr int NW = 2 * NCH;
         constexpr int NF = FRI * FRJ;
-        const char* P = smem + (kt & 1) * LY::STAGE;
+        if constexpr (MORE) dma_stage(kt + 1, N);
+        if constexpr (!MORE) dma_atile(0, N);
 #pragma unroll
         for (int ks = 0; ks < BK / 16 - 1; ++ks) {
             const int set = ks & 1;
-            read_frags(P, ks + 1, set ^ 1);
-            // the next stage's global loads are spread over sub-steps 0 and 1
-            if constexpr (MORE) {
-                if (ks == 0) load_stage((kt + 1) * BK, 1);
-                if (ks == 1) load_stage((kt + 1) * BK, 2);
-            }
+            read_frags(S, ks + 1, set ^ 1);
             mfma_block(set, 0, NF);
-            // interleave: one MFMA, then one LDS read / global load
+            // interleave: one MFMA, then one LDS read (and in sub-step 0 one load)
 #pragma unroll
             for (int i = 0; i < NF; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 if (i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (MORE && ks < 2 && i < NCH) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (MORE && ks == 0 && i < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         }
-        // last sub-step: half its MFMAs carry the next stage's LDS writes; the
-        // barrier comes next, and the next stage's first fragment reads run
-        // under the other half
+        // last sub-step: the barrier sits in the middle of its MFMAs, and the
+        // next stage's first fragment reads run under the second half
         constexpr int SL = (BK / 16 - 1) & 1;
         if constexpr (MORE) {
-            store_stage((kt & 1) ^ 1);
             mfma_block(SL, 0, NF / 2);
-#pragma unroll
-            for (int i = 0; i < NF / 2; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (i < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-            }
-            if (NW > NF / 2) __builtin_amdgcn_sched_group_barrier(0x200, NW - NF / 2, 0);
+            wait_vm0();
             __syncthreads();
-            read_frags(smem + ((kt + 1) & 1) * LY::STAGE, 0, 0);
+            read_frags(N, 0, 0);
             mfma_block(SL, NF / 2, NF);
 #pragma unroll
             for (int i = 0; i < NF / 2; ++i) {
@@ -266,12 +296,18 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     };
 
     const int nk = K / BK;
-    load_stage(0, 3);
-    store_stage(0);
+    dma_stage(0, smem);
+    wait_vm0();
     __syncthreads();
     read_frags(smem, 0, 0);
-    for (int kt = 0; kt < nk - 1; ++kt) stage(kt, std::true_type{});
-    stage(nk - 1, std::false_type{});
+    for (int kt = 0; kt < nk - 1; ++kt)
+        stage(smem + (kt & 1) * LY::STAGE, smem + ((kt + 1) & 1) * LY::STAGE, kt, std::true_type{});
+    stage(smem + ((nk - 1) & 1) * LY::STAGE, smem + (nk & 1) * LY::STAGE, nk - 1, std::false_type{});
+    if constexpr (MODE == NS_POLY) {
+        if (T > 128) dma_atile(1, smem + ((nk - 1) & 1) * LY::STAGE);
+        wait_vm0();
+        __syncthreads();
+    }
 
     // ---------------- epilogue (lane holds C[i][j .. j+3]) ----------------
     float alpha = 1.0f;
@@ -296,38 +332,17 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
 
     // Output tiles are staged in LDS as bf16 rows of EROW bytes (2T + 8: 32
     // consecutive rows start in distinct 8-byte bank slots) and leave as
-    // whole cache lines; the polynomial's A tile comes in the same way.
-    constexpr int EROW = 2 * T + 8;
-    static_assert(T * EROW <= 2 * LY::STAGE, "staged tile must fit in LDS");
+    // whole cache lines.
     auto lds64 = [&](int off) -> uint2& { return *reinterpret_cast<uint2*>(smem + off); };
-
-    if (MODE == NS_POLY) {
-        const bf16* Asrc = ain + d.a_off + (int64_t)i0 * d.m_pad + j0;
-        const __amdgpu_buffer_rsrc_t ra = rsrc(Asrc, (uint32_t)(T * d.m_pad * 2));
-        constexpr int CPR = T / 8;                   // 16-byte chunks per row
-        constexpr int NE = T * CPR / NT;             // chunks per thread
-        const int er = tid / CPR, ec = tid % CPR;
-        constexpr int RSTEP = NT / CPR;
-#pragma unroll
-        for (int b0 = 0; b0 < NE; b0 += NCH) {
-#pragma unroll
-            for (int q = 0; q < NCH; ++q)
-                preg[q] = bload(ra, er * d.m_pad * 2 + ec * 16, (b0 + q) * RSTEP * d.m_pad * 2);
-#pragma unroll
-            for (int q = 0; q < NCH; ++q) {
-                const int off = (er + (b0 + q) * RSTEP) * EROW + ec * 16;
-                lds64(off) = make_uint2(preg[q].x, preg[q].y);
-                lds64(off + 8) = make_uint2(preg[q].z, preg[q].w);
-            }
-        }
-        __syncthreads();
-    }
 
     float rsq[FRI];
 #pragma unroll
     for (int f = 0; f < FRI; ++f) rsq[f] = 0.f;
 
     uint2 ev[FRI][FRJ][4];
+    // POLY: lane's A entries A[il][jl .. jl+3] (il & 15 == l32 & 15)
+    const char* abase = smem + ((nk + (wi * WTM) / 128) & 1) * LY::STAGE + ((wi * WTM) % 128 + l32) * LY::XROWB + 8 * hi;
+    const int asw = l32 & 15;
 #pragma unroll
     for (int fi = 0; fi < FRI; ++fi) {
         const int il = wi * WTM + fi * 32 + l32;
@@ -341,7 +356,9 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
                 for (int e = 0; e < 4; ++e) v[e] = acc[fi][fj][4 * g + e];
                 if (MODE == NS_POLY) {
                     // P = a I + b A + c A A: the a X term of the update rides on P's diagonal
-                    const uint2 in = lds64(il * EROW + 2 * jl);
+                    const int c = ((wj * WTN + fj * 32) >> 3) + g;
+                    const uint2 in =
+                        *reinterpret_cast<const uint2*>(abase + fi * 32 * LY::XROWB + 16 * (c ^ asw));
                     v[0] = fmaf(cb, bf16_lo(in.x), cc * v[0]);
                     v[1] = fmaf(cb, bf16_hi(in.x), cc * v[1]);
                     v[2] = fmaf(cb, bf16_lo(in.y), cc * v[2]);
@@ -369,7 +386,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             }
         }
     }
-    if (MODE == NS_POLY) __syncthreads();  // the staged A tile is read; LDS is reused below
+    if (MODE == NS_POLY) __syncthreads();  // the A tile is read; LDS is reused below
 #pragma unroll
     for (int fi = 0; fi < FRI; ++fi)
 #pragma unroll

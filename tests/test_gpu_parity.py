@@ -39,6 +39,7 @@ RAGGED = [
     (96, 160, 1, "gauss", 1.0, 1),  # frozen
     (33, 257, 1, "student_t", 0.0),  # lr_mul 0: params unchanged, momentum advances
     (384, 768, 1, "spike", 2.0),  # several tiles, lr_mul 2
+    (1000, 700, 1, "spike"),      # tall, 256-tiles with a padded edge (768 x 1024)
 ]
 
 
@@ -91,10 +92,11 @@ def test_ragged_fp32_all_stages():
 
 def test_heavy_ball_and_weight_decay_and_steps():
     # heavy-ball momentum, Nesterov off, decoupled weight decay, 7 NS steps with
-    # a per-iteration coefficient schedule
+    # a per-iteration coefficient schedule whose last step is the cubic
+    # Newton-Schulz step (c = 0: the polynomial has no A A term)
     w = custom_workload(103, [(150, 300, 1, "gauss", 1.5), (300, 150, 1, "gauss")], steps=2,
                         weight_decay=0.1, nesterov=0, ns_steps=7, lr=0.03)
-    coeffs = [(3.4445, -4.7750, 2.0315)] * 5 + [(2.0, -1.5, 0.5)] * 2
+    coeffs = [(3.4445, -4.7750, 2.0315)] * 5 + [(2.0, -1.5, 0.5), (1.5, -0.5, 0.0)]
     run = GpuRun(w, momentum_kind=B.MUON_MOMENTUM_HEAVY_BALL, coeffs=coeffs)
     orc = O.OracleMuon(w.entries, w.total, momentum=w.momentum, nesterov=0, coeffs=coeffs,
                        weight_decay=0.1, momentum_kind="heavy_ball", mode="bf16")
