@@ -21,6 +21,19 @@ namespace muon {
 namespace {
 
 constexpr int TS = kEwTile;  // 64
+// Streams that are touched once per step (gradients, momentum, parameters,
+// the Newton–Schulz output) use nontemporal loads / stores, so they do not
+// push the Newton–Schulz working set out of L2 and the MALL; only X~, which
+// the Gram kernel reads next, is stored normally.
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ntld4(const float* p) {
+    const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void ntst4(float* p, float4 v) {
+    f4v w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<f4v*>(p));
+}
 
 struct TileCoord {
     int mi, i0, j0;
@@ -69,7 +82,9 @@ __device__ __forceinline__ void load_x4(const XT* src, float* v);
 
 template <>
 __device__ __forceinline__ void load_x4<bf16>(const bf16* src, float* v) {
-    const uint2 w = *reinterpret_cast<const uint2*>(src);
+    typedef unsigned u2v __attribute__((ext_vector_type(2)));
+    const u2v wv = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(src));
+    const uint2 w = make_uint2(wv.x, wv.y);
     v[0] = bf16_lo(w.x);
     v[1] = bf16_hi(w.x);
     v[2] = bf16_lo(w.y);
@@ -118,13 +133,13 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MatDesc* __restrict
             if (i < d.m) {
                 const int64_t base = d.p_off + (int64_t)i * d.C + j;
                 if (d.vec_ok && j + 3 < d.n) {
-                    const float4 g4 = *reinterpret_cast<const float4*>(grads + base);
-                    float4 m4 = *reinterpret_cast<const float4*>(mom + base);
+                    const float4 g4 = ntld4(grads + base);
+                    float4 m4 = ntld4(mom + base);
                     u[0] = mom_update(g4.x, m4.x, P);
                     u[1] = mom_update(g4.y, m4.y, P);
                     u[2] = mom_update(g4.z, m4.z, P);
                     u[3] = mom_update(g4.w, m4.w, P);
-                    *reinterpret_cast<float4*>(mom + base) = m4;
+                    ntst4(mom + base, m4);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -153,13 +168,13 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MatDesc* __restrict
             if (r < d.R) {
                 const int64_t base = d.p_off + (int64_t)r * d.C + c;
                 if (d.vec_ok && c + 3 < d.C) {
-                    const float4 g4 = *reinterpret_cast<const float4*>(grads + base);
-                    float4 m4 = *reinterpret_cast<const float4*>(mom + base);
+                    const float4 g4 = ntld4(grads + base);
+                    float4 m4 = ntld4(mom + base);
                     u[0] = mom_update(g4.x, m4.x, P);
                     u[1] = mom_update(g4.y, m4.y, P);
                     u[2] = mom_update(g4.z, m4.z, P);
                     u[3] = mom_update(g4.w, m4.w, P);
-                    *reinterpret_cast<float4*>(mom + base) = m4;
+                    ntst4(mom + base, m4);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -224,12 +239,12 @@ __global__ __launch_bounds__(kThreads) void k_apply(const MatDesc* __restrict__ 
             const float coef = fr ? coef0 * fr[d.row_off + i] : coef0;
             const int64_t base = d.p_off + (int64_t)i * d.C + j;
             if (d.vec_ok && j + 3 < d.n) {
-                float4 p4 = *reinterpret_cast<float4*>(params + base);
+                float4 p4 = ntld4(params + base);
                 p4.x = fmaf(-coef, x[0], p4.x * decay);
                 p4.y = fmaf(-coef, x[1], p4.y * decay);
                 p4.z = fmaf(-coef, x[2], p4.z * decay);
                 p4.w = fmaf(-coef, x[3], p4.w * decay);
-                *reinterpret_cast<float4*>(params + base) = p4;
+                ntst4(params + base, p4);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -265,12 +280,12 @@ __global__ __launch_bounds__(kThreads) void k_apply(const MatDesc* __restrict__ 
             if (r >= d.R) continue;
             const int64_t base = d.p_off + (int64_t)r * d.C + c;
             if (d.vec_ok && c + 3 < d.C) {
-                float4 p4 = *reinterpret_cast<float4*>(params + base);
+                float4 p4 = ntld4(params + base);
                 p4.x = fmaf(-coef[0], lds[rl][cg], p4.x * decay);
                 p4.y = fmaf(-coef[1], lds[rl][cg + 1], p4.y * decay);
                 p4.z = fmaf(-coef[2], lds[rl][cg + 2], p4.z * decay);
                 p4.w = fmaf(-coef[3], lds[rl][cg + 3], p4.w * decay);
-                *reinterpret_cast<float4*>(params + base) = p4;
+                ntst4(params + base, p4);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
