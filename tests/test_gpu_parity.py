@@ -71,7 +71,7 @@ def _run_all_stages(w, steps, **hp):
         sl = slice(off, off + r * c)
         if e.frozen:
             assert np.array_equal(p[sl], p0[sl]) and np.all(mom[sl] == 0)
-        elif e.lr_mul == 0.0 or e.gclass == "zero":
+        elif e.lr_mul == 0.0 or (e.gclass == "zero" and w.weight_decay == 0.0):
             assert np.array_equal(p[sl], p0[sl])
             if e.gclass != "zero":
                 assert np.any(mom[sl] != 0)
@@ -82,6 +82,24 @@ def _run_all_stages(w, steps, **hp):
 @pytest.mark.parametrize("normuon", [0, 1])
 def test_ragged_bf16_all_stages(normuon):
     w = custom_workload(100 + normuon, RAGGED, steps=3, normuon=normuon, lr=0.05)
+    _run_all_stages(w, 3)
+
+
+# every matrix on 128 / 256 tiles, decoupled weight decay with per-matrix
+# lr_mul / wd_mul, ragged edges, transposed blocks, zero and frozen matrices
+LARGE_TILES = [
+    (200, 300, 1, "spike", 1.5, 0, 0.5),
+    (300, 200, 1, "spike", 1.0, 0, 2.0),  # tall -> transposed
+    (1000, 700, 1, "spike"),              # 256-tiles, transposed, padded edge
+    (130, 130, 1, "zero"),
+    (96, 160, 1, "gauss", 1.0, 1),        # frozen
+    (65, 131, 1, "student_t", 0.0),       # lr_mul 0
+    (129, 67, 2, "gauss"),                # odd widths: scalar edge path
+]
+
+
+def test_weight_decay_large_tiles_ragged():
+    w = custom_workload(109, LARGE_TILES, steps=3, lr=0.05, weight_decay=0.1)
     _run_all_stages(w, 3)
 
 

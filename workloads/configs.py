@@ -154,7 +154,7 @@ def custom_workload(
     steps: int = 3,
     **hp,
 ) -> Workload:
-    """A workload from (rows, cols[, count[, gclass[, lr_mul[, frozen]]]]) tuples.
+    """A workload from (rows, cols[, count[, gclass[, lr_mul[, frozen[, wd_mul]]]]]) tuples.
 
     Used for parity cases with ragged edges, degenerate shapes and mixed
     classes at sizes the oracle finishes in seconds.
@@ -167,7 +167,8 @@ def custom_workload(
         gclass = s[3] if len(s) > 3 else "spike"
         lr_mul = float(s[4]) if len(s) > 4 else 1.0
         frozen = int(s[5]) if len(s) > 5 else 0
-        entries.append(Entry(rows, cols, count, off, lr_mul=lr_mul, frozen=frozen,
+        wd_mul = float(s[6]) if len(s) > 6 else 1.0
+        entries.append(Entry(rows, cols, count, off, lr_mul=lr_mul, wd_mul=wd_mul, frozen=frozen,
                              name=f"m{len(entries)}", gclass=gclass))
         off += rows * cols * count
     return Workload(config_id, f"custom{config_id}", entries, steps=steps, **hp)
