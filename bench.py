@@ -33,7 +33,8 @@ GRAD_POOL = 4               # distinct gradient sets cycled through the timed st
 
 def _kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("kernels_ns.hip", "kernels_ns_mfma.hip", "kernels_elementwise.hip", "kernel_common.hpp",
+    for f in ("kernels_ns.hip", "kernels_ns_mfma.hip", "kernels_ns_small.hip", "kernels_elementwise.hip",
+              "kernel_common.hpp",
               "device_types.hpp", "plan.cpp", "api.cpp"):
         with open(os.path.join(ROOT, "muon_newton_schulz_04_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
@@ -100,6 +101,8 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str) -> dict:
             elif "k_ns_big<" in name or "k_ns<" in name:
                 mode = name.split("<", 1)[1].split(">", 1)[0].split(",")
                 key = {"0": "gram", "1": "poly", "2": "update"}[mode[-2].strip() if "big" in name else mode[2].strip()]
+            elif "k_ns_small" in name:
+                key = "ns_small"
             elif "k_momentum" in name:
                 key = "momentum"
             elif "k_apply" in name:
@@ -245,7 +248,8 @@ def main() -> int:
     ms = start.elapsed_time(stop) / args.steps
     assert np.isfinite(params[:1000].cpu().numpy()).all()
 
-    ns_flops = work.flops[B.MUON_KERNEL_GRAM] + work.flops[B.MUON_KERNEL_POLY] + work.flops[B.MUON_KERNEL_UPDATE]
+    ns_flops = (work.flops[B.MUON_KERNEL_GRAM] + work.flops[B.MUON_KERNEL_POLY] + work.flops[B.MUON_KERNEL_UPDATE]
+                + work.flops[B.MUON_KERNEL_NS_SMALL])
     value = ns_flops / (ms * 1e-3) / 1e12
     fp32 = w.ns_precision == "fp32"
     peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
@@ -265,7 +269,7 @@ def main() -> int:
                 entry["gbs"] = work.bytes[k] / lps / (per_launch_ms * 1e-3) / 1e9
             kernels[name] = entry
         B.muon_profile_read(H.h, 0, 1)
-    ns_ms = sum(kernels.get(k, {}).get("ms_per_step", 0.0) for k in ("gram", "poly", "update"))
+    ns_ms = sum(kernels.get(k, {}).get("ms_per_step", 0.0) for k in ("gram", "poly", "update", "ns_small"))
     roofline = None
     if kernels:
         dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])

@@ -188,7 +188,9 @@ enum {
     MUON_KERNEL_UPDATE = 3,   /* X <- a X + B X */
     MUON_KERNEL_NORMUON = 4,  /* NorMuon row factors */
     MUON_KERNEL_APPLY = 5,    /* parameter update */
-    MUON_KERNEL_COUNT = 6
+    MUON_KERNEL_NS_SMALL = 6, /* every Newton-Schulz iteration of the bf16 matrices whose
+                               * short side is at most 64 (one workgroup per matrix) */
+    MUON_KERNEL_COUNT = 7
 };
 
 /* Algorithmic work of one muon_step for this plan (frozen matrices excluded).

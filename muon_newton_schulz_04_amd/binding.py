@@ -44,8 +44,9 @@ MUON_KERNEL_POLY = 2
 MUON_KERNEL_UPDATE = 3
 MUON_KERNEL_NORMUON = 4
 MUON_KERNEL_APPLY = 5
-MUON_KERNEL_COUNT = 6
-KERNEL_NAMES = ["momentum", "gram", "poly", "update", "normuon", "apply"]
+MUON_KERNEL_NS_SMALL = 6
+MUON_KERNEL_COUNT = 7
+KERNEL_NAMES = ["momentum", "gram", "poly", "update", "normuon", "apply", "ns_small"]
 
 
 class muon_matrix(ctypes.Structure):

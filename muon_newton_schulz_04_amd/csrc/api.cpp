@@ -207,6 +207,7 @@ muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, co
     e = up(P.off_mats, P.mats.data(), P.mats.size() * sizeof(muon::MatDesc));
     if (e == hipSuccess) e = up(P.off_ewmap, P.ew_map.data(), P.ew_map.size() * 4);
     if (e == hipSuccess) e = up(P.off_active, P.active.data(), P.active.size() * 4);
+    if (e == hipSuccess) e = up(P.off_small, P.small.data(), P.small.size() * 4);
     for (const auto& L : P.lists) {
         if (e == hipSuccess) e = up(L.off_gram, L.gram.data(), L.gram.size() * sizeof(muon::TileWork));
         if (e == hipSuccess) e = up(L.off_poly, L.poly.data(), L.poly.size() * sizeof(muon::TileWork));
@@ -278,6 +279,17 @@ muon_status muon_step(muon_handle* h, float* params, const float* grads, float* 
     if (s != MUON_OK) return s;
 
     const int steps = P.hp.ns_steps;
+    if (!P.small.empty()) {
+        muon::NsCoeffs co{};
+        std::memcpy(co.c, P.hp.ns_coeffs, sizeof(co.c));
+        co.steps = steps;
+        co.eps = P.hp.ns_eps;
+        s = run(MUON_KERNEL_NS_SMALL, "small-matrix Newton-Schulz kernel", [&] {
+            return muon::launch_ns_small(L, reinterpret_cast<const int32_t*>(h->ws + P.off_small), (int)P.small.size(),
+                                         P.small_np, co, ns_out(h), P.hp.normuon);
+        });
+        if (s != MUON_OK) return s;
+    }
     for (int k = 0; k < steps; ++k) {
         void* xin = k == 0 ? L.xt : ((k & 1) ? L.x1 : L.x0);
         void* xout = k == 0 ? L.x1 : ((k & 1) ? L.x0 : L.x1);
@@ -396,9 +408,14 @@ muon_status muon_work_stats(const muon_handle* h, muon_work* out) {
     for (int32_t mi : P.active) {
         const muon::MatDesc& d = P.mats[mi];
         const double m = d.m, n = d.n;
-        out->flops[MUON_KERNEL_GRAM] += steps * m * (m + 1) * n;
-        out->flops[MUON_KERNEL_POLY] += steps * m * (m + 1) * m;
-        out->flops[MUON_KERNEL_UPDATE] += steps * 2.0 * m * m * n;
+        const double f_gram = steps * m * (m + 1) * n, f_poly = steps * m * (m + 1) * m, f_upd = steps * 2.0 * m * m * n;
+        if (P.is_small(d)) {
+            out->flops[MUON_KERNEL_NS_SMALL] += f_gram + f_poly + f_upd;
+        } else {
+            out->flops[MUON_KERNEL_GRAM] += f_gram;
+            out->flops[MUON_KERNEL_POLY] += f_poly;
+            out->flops[MUON_KERNEL_UPDATE] += f_upd;
+        }
         act += (int64_t)d.m * d.n;
         rows += m;
         rowpart += (double)(d.n_pad / d.T) * m;
@@ -413,6 +430,7 @@ muon_status muon_work_stats(const muon_handle* h, muon_work* out) {
     out->launches[MUON_KERNEL_GRAM] = steps * nl;
     out->launches[MUON_KERNEL_POLY] = steps * nl;
     out->launches[MUON_KERNEL_UPDATE] = steps * nl;
+    out->launches[MUON_KERNEL_NS_SMALL] = P.small.empty() ? 0 : 1;
     out->launches[MUON_KERNEL_NORMUON] = P.hp.normuon ? any : 0;
     out->launches[MUON_KERNEL_APPLY] = any;
     return MUON_OK;

@@ -6,13 +6,16 @@
 
 namespace muon {
 
-// Tile sizes. GEMM tiles are square T x T with T in {64, 128}; every
+// Tile sizes. GEMM tiles are square T x T with T in {64, 128, 256}; every
 // canonical buffer is padded to a multiple of its bucket's T in both
 // dimensions (zero-filled padding keeps Newton–Schulz exact on the valid
 // block, so the GEMM kernels carry no bounds checks). Elementwise kernels
 // work on 64 x 64 tiles of the padded canonical frame.
 constexpr int kEwTile = 64;
 constexpr int kThreads = 256;
+// bf16 matrices with m_pad = 64 and n_pad <= kSmallMaxNPad run every
+// Newton–Schulz iteration in one workgroup (X, A, P resident in LDS).
+constexpr int kSmallMaxNPad = 512;
 
 // One (sub-)matrix of the table, in both frames.
 //   stored frame:    [R, C] row-major at p_off in params / grads / momentum

@@ -45,6 +45,13 @@ struct GemmList {
 
 enum NsMode { NS_GRAM = 0, NS_POLY = 1, NS_UPDATE = 2 };
 
+// Per-iteration Newton–Schulz coefficients (a, b, c) and the normalisation eps.
+struct NsCoeffs {
+    float c[16][3];
+    int steps;
+    float eps;
+};
+
 hipError_t launch_momentum(const LaunchCtx& L, const float* grads, float* mom, float beta, int nesterov,
                            int heavy);
 hipError_t launch_apply(const LaunchCtx& L, const void* xo, const float* f, float* params, float lr, float wd);
@@ -63,5 +70,13 @@ hipError_t launch_ns_stage(const LaunchCtx& L, const GemmList& G, int mode, cons
 // The same stage with the bf16 large-tile kernels (T = 128 or 256).
 hipError_t launch_ns_stage_big(const LaunchCtx& L, const GemmList& G, int mode, const void* xin, const void* ain,
                                void* out, float ca, float cb, float cc, int first, float eps, int rowstats);
+
+// Every iteration of the bf16 Newton–Schulz for the small matrices in `list`
+// (m_pad = 64, n_pad <= n_pad_max <= 512), one workgroup per matrix, reading
+// X~ and writing the output to `out` (same padded canonical layout); with
+// rowstats, also the NorMuon row partial sums.
+hipError_t launch_ns_small(const LaunchCtx& L, const int32_t* list, int n, int n_pad_max, const NsCoeffs& co,
+                           void* out, int rowstats);
+size_t ns_small_lds_bytes(int n_pad_max);
 
 }  // namespace muon

@@ -231,6 +231,11 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
         for (int32_t mi : P.active) {
             const MatDesc& d = P.mats[mi];
             if (d.T != T) continue;
+            if (P.is_small(d)) {
+                P.small.push_back(mi);
+                P.small_np = std::max(P.small_np, d.n_pad);
+                continue;
+            }
             const int tm = d.m_pad / T, tn = d.n_pad / T;
             std::vector<TileWork> gl, ul;
             for (int ti = 0; ti < tm; ++ti)
@@ -243,7 +248,7 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
             cp.push_back(d.m_pad);
             cu.push_back(d.m_pad);
         }
-        if (g.empty()) continue;
+        if (g.empty()) continue;  // (also when every matrix of this size is small)
         TileList L;
         L.T = T;
         L.gram = order_for_xcds(g, cg);
@@ -275,6 +280,7 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
     P.off_mats = take(nmats * sizeof(MatDesc));
     P.off_ewmap = take(P.ew_map.size() * 4);
     P.off_active = take(P.active.size() * 4);
+    P.off_small = take(P.small.size() * 4);
     for (auto& L : P.lists) {
         L.off_gram = take(L.gram.size() * sizeof(TileWork));
         L.off_poly = take(L.poly.size() * sizeof(TileWork));

@@ -28,6 +28,9 @@ struct Plan {
     std::vector<int32_t> active;        // active matrix indices
     std::vector<int32_t> ew_map;        // elementwise tile -> matrix
     std::vector<TileList> lists;        // one per tile size in use
+    std::vector<int32_t> small;         // active matrices of the one-workgroup Newton–Schulz
+    int small_np = 0;                   // their largest n_pad
+    size_t off_small = 0;
     int64_t extent = 0;                 // elements the flat buffers must hold
     int64_t x_elems = 0, a_elems = 0, rows_total = 0, rowpart_elems = 0;
     // workspace byte offsets
@@ -38,6 +41,7 @@ struct Plan {
     size_t total_bytes = 0;
     // 64-bit sums used by tools and tests
     double ns_alg_flops = 0.0;          // per step, symmetric products counted as m(m+1)k
+    bool is_small(const MatDesc& d) const { return esize == 2 && d.T == 64 && d.n_pad <= kSmallMaxNPad; }
 };
 
 // Validate and build. Returns MUON_OK or an error code with *err set.
