@@ -46,11 +46,20 @@ namespace {
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BK = 64;       // k per LDS stage
-constexpr int KROWB = 128;   // bytes per row of a k-contiguous tile (BK bf16, swizzled)
+// K pipeline per stage kind: BK-wide K slices through NBUF LDS buffers, the
+// loads of slice kt + NBUF - 1 going out while slice kt is read. The Gram
+// (long K: 3072 for a 768 x 3072 X) hides L2-miss latency with four 32-wide
+// slices; the polynomial and the update (K = m_pad) do better with two
+// 64-wide slices (half the barriers, a shorter prologue).
+template <int MODE>
+struct Pipe {
+    static constexpr int BK = MODE == NS_GRAM ? 32 : 64;
+    static constexpr int NBUF = MODE == NS_GRAM ? 4 : 2;
+};
 
-template <int T>
+template <int T, int BK>
 struct Layout {
+    static constexpr int KROWB = 2 * BK;                // bytes per row of a k-contiguous tile (swizzled)
     static constexpr int XROWB = 2 * T;                 // bytes per row of the X tile (swizzled)
     static constexpr int KTILE = T * KROWB;             // k-contiguous tile, one stage
     static constexpr int STAGE = 2 * KTILE;             // P tile + (k-contiguous Q or X) tile
@@ -65,9 +74,19 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int voff, int s
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// 16 bytes per lane, global -> LDS: lane i lands at lds + 16 i (lds is wave-uniform)
+// 16 bytes per lane, global -> LDS: lane i lands at lds + 16 i (lds is
+// wave-uniform, passed in M0). Issued as inline assembly so that the compiler
+// does not track these LDS writes: it would otherwise wait for every load in
+// flight (vmcnt(0)) before LDS reads it cannot prove disjoint, which undoes
+// the ring; the kernel orders the ring itself with explicit vmcnt waits and
+// barriers, and every such load has completed before any compiler-managed
+// vector memory wait (the epilogue) is reached. No other code of this kernel
+// uses M0.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(LDS_AS char*)lds, 16, voff, soff, 0, 0);
+    const uint32_t m0v = (uint32_t)(uintptr_t)(LDS_AS char*)lds;
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "s"(m0v));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -92,9 +111,13 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     constexpr int WTN = T / WN;
     constexpr int FRI = WTM / 32;
     constexpr int FRJ = WTN / 32;
-    using LY = Layout<T>;
+    constexpr int BK = Pipe<MODE>::BK;
+    constexpr int NBUF = Pipe<MODE>::NBUF;
+    constexpr int D = NBUF - 1;                      // prefetch distance in slices
+    using LY = Layout<T, BK>;
+    constexpr int KROWB = LY::KROWB;
     constexpr int EROW = 2 * T + 8;                  // epilogue staging row (bytes)
-    constexpr int SMEM = 2 * LY::STAGE > T * EROW ? 2 * LY::STAGE : T * EROW;
+    constexpr int SMEM = NBUF * LY::STAGE > T * EROW ? NBUF * LY::STAGE : T * EROW;
     static_assert(FRJ >= 1 && NWV % 2 == 0, "tile too small for this wave grid");
 
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -140,22 +163,29 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         rsrc(Qsrc, (uint32_t)((MODE == NS_UPDATE ? K * ldq : T * ldq) * 2));
 
     // ---- direct-to-LDS load geometry ----
-    // k-contiguous tile: instruction q of wave w fills rows q KROUND + 8 w .. +7;
-    // lane l takes physical chunk l & 7 of row 8 w + (l >> 3), i.e. logical chunk
-    // (l & 7) ^ ((row >> 1) & 7) (q KROUND is a multiple of 16: same swizzle)
-    constexpr int KROUND = 8 * NWV;
+    // k-contiguous tile (KROWB-byte rows of CPRK 16-byte chunks): instruction
+    // q of wave w fills rows q KROUND + RPI w .. +RPI-1; lane l takes physical
+    // chunk l % CPRK of row RPI w + l / CPRK, i.e. logical chunk
+    // (l % CPRK) ^ ((row >> SH) & (CPRK - 1)); with 2^SH = 16 / CPRK the 16
+    // rows of a ds_read_b128 phase land in 16 distinct 16-byte bank slots
+    constexpr int CPRK = KROWB / 16;
+    constexpr int RPI = 64 / CPRK;
+    constexpr int SH = CPRK == 8 ? 1 : 2;
+    static_assert(CPRK == 8 || CPRK == 4, "slice width");
+    constexpr int KROUND = RPI * NWV;
     constexpr int NKI = T / KROUND;
-    const int kr = wave * 8 + (lane >> 3);
-    const int kc = (lane & 7) ^ ((kr >> 1) & 7);
+    const int kr = wave * RPI + lane / CPRK;
+    const int kc = (lane % CPRK) ^ ((kr >> SH) & (CPRK - 1));
     const int vp = kr * ldp * 2 + kc * 16;
     const int vqk = kr * ldq * 2 + kc * 16;
-    // X tile (update): XRPI rows of XCH chunks per instruction; lane l takes
-    // physical chunk l % XCH of row w XRPI + l / XCH, logical chunk ^ 4 (row & 3)
+    // X tile (update) and the polynomial's A tile (2T-byte rows): XRPI rows of
+    // XCH chunks per instruction; lane l takes physical chunk l % XCH of row
+    // w XRPI + l / XCH
     constexpr int XCH = T / 8;
     constexpr int XRPI = 64 / XCH;
     constexpr int XROUND = XRPI * NWV;
     constexpr int NXI = BK / XROUND;
-    static_assert(NKI >= 1 && NXI >= 1 && XROUND % 4 == 0, "load geometry");
+    static_assert(NKI >= 1 && NXI >= 1 && XROUND == 16, "load geometry");
     const int xr = wave * XRPI + lane / XCH;
     const int xc = (lane % XCH) ^ (4 * (xr & 3));
     const int vqx = xr * ldq * 2 + xc * 16;
@@ -163,7 +193,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     auto dma_stage = [&](int kt, char* S) {
         const int k0 = kt * BK;
 #pragma unroll
-        for (int q = 0; q < NKI; ++q) dma16(rp, S + (q * KROUND + wave * 8) * KROWB, vp, (q * KROUND * ldp + k0) * 2);
+        for (int q = 0; q < NKI; ++q) dma16(rp, S + (q * KROUND + wave * RPI) * KROWB, vp, (q * KROUND * ldp + k0) * 2);
         if (MODE == NS_UPDATE) {
 #pragma unroll
             for (int q = 0; q < NXI; ++q)
@@ -171,9 +201,21 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         } else if (!same) {
 #pragma unroll
             for (int q = 0; q < NKI; ++q)
-                dma16(rq, S + LY::KTILE + (q * KROUND + wave * 8) * KROWB, vqk, (q * KROUND * ldq + k0) * 2);
+                dma16(rq, S + LY::KTILE + (q * KROUND + wave * RPI) * KROWB, vqk, (q * KROUND * ldq + k0) * 2);
         }
     };
+    // load instructions one stage issues (a diagonal Gram / poly tile loads one operand)
+    constexpr int NDMA = NKI + (MODE == NS_UPDATE ? NXI : NKI);
+    constexpr int NDMA_SAME = NKI;
+    // wait until at most `stages` later stages' loads are still in flight
+    auto wait_stage = [&](auto stages_c) {
+        constexpr int ST = decltype(stages_c)::value;
+        if (MODE != NS_UPDATE && same)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (ST * NDMA_SAME));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (ST * NDMA));
+    };
+    static_assert((D - 1) * NDMA < 16, "vmcnt immediate");
 
     f32x16 acc[FRI][FRJ];
 #pragma unroll
@@ -187,7 +229,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     // k-contiguous: lane reads row l32 of a 32-row block, logical chunk 2 ks + hi
     int fo[BK / 16];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) fo[ks] = l32 * KROWB + 16 * ((2 * ks + hi) ^ ((l32 >> 1) & 7));
+    for (int ks = 0; ks < BK / 16; ++ks) fo[ks] = l32 * KROWB + 16 * ((2 * ks + hi) ^ ((l32 >> SH) & (CPRK - 1)));
     const int pb = wi * WTM * KROWB;
     const int qb = wj * WTN * KROWB + (same ? 0 : LY::KTILE);
     // X (update): lane s of 16-lane group g reads row 8 (g >> 1) + (s >> 2) (+ 16 ks + 4 h),
@@ -220,27 +262,26 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         }
     };
     // POLY: the output tile's own A block (for the b A term) comes into LDS as
-    // 2T-byte rows, 128 rows per stage buffer, chunk c of row r at c ^ (r & 15);
-    // rows [0, 128) go to the buffer the last K slice leaves free, the rest
-    // (T = 256) to the other one once that slice is done
-    constexpr int AQ = 128 / XROUND;  // load instructions per 128 rows
+    // 2T-byte rows, ARPB rows per stage buffer, chunk c of row r at c ^ (r & 15);
+    // part q (rows q ARPB ..) goes to buffer (nk + q) % NBUF: parts 0 .. NBUF-2
+    // load during the last K slice (into the buffers it leaves free), the
+    // last part (T = 256) once that slice is done
+    constexpr int ARPB = LY::STAGE / LY::XROWB;
+    constexpr int NAP = T / ARPB;
+    static_assert(MODE != NS_POLY || (T % ARPB == 0 && NAP <= NBUF), "A tile layout");
     const int ar = wave * XRPI + lane / XCH;
     const int va = ar * d.m_pad * 2 + ((lane % XCH) ^ (ar & 15)) * 16;
-    auto dma_atile = [&](int part, char* buf) {
+    auto dma_apart = [&](int part, char* buf) {
         if constexpr (MODE == NS_POLY) {
             const __amdgpu_buffer_rsrc_t ra =
                 rsrc(ain + d.a_off + (int64_t)i0 * d.m_pad + j0, (uint32_t)(T * d.m_pad * 2));
 #pragma unroll
-            for (int q = 0; q < AQ; ++q) {
-                const int row = part * 128 + q * XROUND;
-                if (row < T) dma16(ra, buf + (q * XROUND + wave * XRPI) * LY::XROWB, va, row * d.m_pad * 2);
-            }
+            for (int q = 0; q < ARPB / XROUND; ++q)
+                dma16(ra, buf + (q * XROUND + wave * XRPI) * LY::XROWB, va, (part * ARPB + q * XROUND) * d.m_pad * 2);
         }
     };
-    static_assert(MODE != NS_POLY || (T % 128 == 0 && 128 * LY::XROWB <= LY::STAGE), "A tile layout");
 
     constexpr int NREAD = FRI + (MODE == NS_UPDATE ? 2 : 1) * FRJ;  // LDS read instructions per sub-step
-    constexpr int NDMA = NKI + (MODE == NS_UPDATE ? NXI : NKI);      // load instructions per stage
 
     auto mfma_block = [&](int set, int lo, int hi_) {
 #pragma unroll
@@ -249,39 +290,41 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[set][fj], pfr[set][fi], acc[fi][fj], 0, 0, 0);
         }
     };
-    // One K stage. MORE: a next stage exists; its loads go out first (the
-    // buffer they fill was released by the barrier that ended the previous
-    // stage). The last stage is peeled so the steady-state loop body has no
-    // branches for the scheduler to stop at.
-    // S: this stage's buffer, N: the other one. Both are restrict so that the
-    // compiler knows the loads into N do not feed this stage's LDS reads and
-    // does not wait for them before each read.
-    auto stage = [&](const char* __restrict__ S, char* __restrict__ N, int kt, auto more_c) {
-        constexpr bool MORE = decltype(more_c)::value;
+    // One K stage (kt) of the NBUF-deep ring. S: its buffer; N1: the next
+    // stage's; NL: the buffer the previous stage released, which receives
+    // stage kt + D (LOAD). WAIT: stages beyond kt + 1 whose loads may still be
+    // in flight at the barrier (D - 1 .. 0), or -1 for the last stage, which
+    // has no barrier to the next. The buffers are restrict (and the loads are
+    // invisible to the compiler) so that no wait is inserted before the reads
+    // of S; the explicit waits and barriers order the ring.
+    constexpr int NKS = BK / 16;  // k16 sub-steps per stage
+    auto stage = [&](const char* __restrict__ S, const char* __restrict__ N1, char* __restrict__ NL, int kt,
+                     auto load_c, auto wait_c) {
+        constexpr bool LOAD = decltype(load_c)::value;
+        constexpr int WAIT = decltype(wait_c)::value;
         constexpr int NF = FRI * FRJ;
-        if constexpr (MORE) dma_stage(kt + 1, N);
-        if constexpr (!MORE) dma_atile(0, N);
+        if constexpr (LOAD) dma_stage(kt + D, NL);
 #pragma unroll
-        for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+        for (int ks = 0; ks < NKS - 1; ++ks) {
             const int set = ks & 1;
             read_frags(S, ks + 1, set ^ 1);
             mfma_block(set, 0, NF);
-            // interleave: one MFMA, then one LDS read (and in sub-step 0 one load)
+            // interleave: one MFMA, then one LDS read
 #pragma unroll
             for (int i = 0; i < NF; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 if (i < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (MORE && ks == 0 && i < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         }
         // last sub-step: the barrier sits in the middle of its MFMAs, and the
         // next stage's first fragment reads run under the second half
-        constexpr int SL = (BK / 16 - 1) & 1;
-        if constexpr (MORE) {
+        constexpr int SL = (NKS - 1) & 1;
+        if constexpr (WAIT >= 0) {
             mfma_block(SL, 0, NF / 2);
-            wait_vm0();
+            __builtin_amdgcn_sched_barrier(0);  // keep these MFMAs ahead of the wait
+            wait_stage(std::integral_constant<int, WAIT>{});
             __syncthreads();
-            read_frags(N, 0, 0);
+            read_frags(N1, 0, 0);
             mfma_block(SL, NF / 2, NF);
 #pragma unroll
             for (int i = 0; i < NF / 2; ++i) {
@@ -290,21 +333,33 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             }
             if (NREAD > NF / 2) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NF / 2, 0);
         } else {
+            if constexpr (MODE == NS_POLY) {
+#pragma unroll
+                for (int q = 0; q < NAP && q < NBUF - 1; ++q) dma_apart(q, smem + ((kt + 1 + q) % NBUF) * LY::STAGE);
+            }
             mfma_block(SL, 0, NF);
             __syncthreads();
         }
     };
 
-    const int nk = K / BK;
-    dma_stage(0, smem);
-    wait_vm0();
+    const int nk = K / BK;  // >= 2 (K >= 128)
+    static_assert(D <= 3, "ring depth");
+    auto buf = [&](int k) { return smem + (k % NBUF) * LY::STAGE; };
+#pragma unroll
+    for (int k = 0; k < D; ++k) dma_stage(k, buf(k));
+    wait_stage(std::integral_constant<int, D - 1>{});
     __syncthreads();
-    read_frags(smem, 0, 0);
-    for (int kt = 0; kt < nk - 1; ++kt)
-        stage(smem + (kt & 1) * LY::STAGE, smem + ((kt + 1) & 1) * LY::STAGE, kt, std::true_type{});
-    stage(smem + ((nk - 1) & 1) * LY::STAGE, smem + (nk & 1) * LY::STAGE, nk - 1, std::false_type{});
+    read_frags(buf(0), 0, 0);
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using CD = std::integral_constant<int, D - 1>;
+    using CL = std::integral_constant<int, -1>;
+    for (int kt = 0; kt < nk - D; ++kt) stage(buf(kt), buf(kt + 1), buf(kt + D), kt, std::true_type{}, CD{});
+    if constexpr (D >= 3) stage(buf(nk - 3), buf(nk - 2), buf(nk), nk - 3, std::false_type{}, C1{});
+    if constexpr (D >= 2) stage(buf(nk - 2), buf(nk - 1), buf(nk + 1), nk - 2, std::false_type{}, C0{});
+    stage(buf(nk - 1), buf(nk), buf(nk + 2), nk - 1, std::false_type{}, CL{});
     if constexpr (MODE == NS_POLY) {
-        if (T > 128) dma_atile(1, smem + ((nk - 1) & 1) * LY::STAGE);
+        if constexpr (NAP == NBUF) dma_apart(NBUF - 1, buf(nk + NBUF - 1));
         wait_vm0();
         __syncthreads();
     }
@@ -341,7 +396,12 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
 
     uint2 ev[FRI][FRJ][4];
     // POLY: lane's A entries A[il][jl .. jl+3] (il & 15 == l32 & 15)
-    const char* abase = smem + ((nk + (wi * WTM) / 128) & 1) * LY::STAGE + ((wi * WTM) % 128 + l32) * LY::XROWB + 8 * hi;
+    // (row il lives in part il / ARPB, at buffer (nk + part) % NBUF; ARPB is a
+    // multiple of 32, so a lane's 32-row blocks stay within one part)
+    constexpr int ARPB_E = LY::STAGE / LY::XROWB;
+    auto abase = [&](int il) -> const char* {
+        return smem + ((nk + il / ARPB_E) % NBUF) * LY::STAGE + (il % ARPB_E) * LY::XROWB + 8 * hi;
+    };
     const int asw = l32 & 15;
 #pragma unroll
     for (int fi = 0; fi < FRI; ++fi) {
@@ -358,7 +418,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
                     // P = a I + b A + c A A: the a X term of the update rides on P's diagonal
                     const int c = ((wj * WTN + fj * 32) >> 3) + g;
                     const uint2 in =
-                        *reinterpret_cast<const uint2*>(abase + fi * 32 * LY::XROWB + 16 * (c ^ asw));
+                        *reinterpret_cast<const uint2*>(abase(il) + 16 * (c ^ asw));
                     v[0] = fmaf(cb, bf16_lo(in.x), cc * v[0]);
                     v[1] = fmaf(cb, bf16_hi(in.x), cc * v[1]);
                     v[2] = fmaf(cb, bf16_lo(in.y), cc * v[2]);
