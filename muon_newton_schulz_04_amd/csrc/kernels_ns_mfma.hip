@@ -4,17 +4,20 @@
 // polynomial epilogue, update), re-tiled for MI355X:
 //  * T x T output per workgroup of 2 x WN waves (T = 256: 8 waves, 2 per
 //    SIMD, each 128 x 64 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16).
-//  * K is staged in slices of 64 through two LDS buffers that are filled
-//    by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): a slice's
-//    loads are issued right after the barrier that frees its buffer, a whole
-//    slice ahead of its use, and no VGPRs or ds_write instructions carry them.
-//    Each load instruction lands 64 x 16 bytes contiguously in LDS, so the
-//    tiles are unpadded and bank conflicts are avoided by swizzling 16-byte
-//    chunks on the global side:
+//  * K is staged in slices through a ring of LDS buffers that are filled
+//    by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): 64-wide
+//    slices in two buffers for the polynomial and the update, 32-wide slices
+//    in four buffers for the Gram (whose K is the long side). A slice's loads
+//    are issued right after the barrier that frees its buffer, one (or
+//    three) slices ahead of its use, and no VGPRs or ds_write instructions
+//    carry them. Each load instruction lands 64 x 16 bytes contiguously in
+//    LDS, so the tiles are unpadded and bank conflicts are avoided by
+//    swizzling 16-byte chunks on the global side:
 //      - operands whose contraction index is contiguous (rows of X for the
-//        Gram, rows of A, rows of B) sit as 128-byte rows; chunk c of row r
-//        is stored at chunk c ^ ((r >> 1) & 7), so the 16 rows a 16-lane
-//        phase of ds_read_b128 touches fall in 16 distinct 16-byte slots;
+//        Gram, rows of A, rows of B) sit as 2 BK-byte rows; chunk c of row r
+//        is stored at chunk c ^ ((r >> 1) & 7) (128-byte rows) or
+//        c ^ ((r >> 2) & 3) (64-byte rows), so the 16 rows a 16-lane phase
+//        of ds_read_b128 touches fall in 16 distinct 16-byte slots;
 //      - the update's X tile (contraction over its rows) sits row-major as
 //        2T-byte rows; chunk c of row r is stored at c ^ (4 (r & 3)), so the
 //        4 rows x 64 bytes a half-wave of ds_read_b64_tr_b16 touches fall in
