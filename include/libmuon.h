@@ -79,7 +79,14 @@ enum { MUON_MOMENTUM_LERP = 0, MUON_MOMENTUM_HEAVY_BALL = 1 };
  *  momentum_kind LERP: m <- beta m + (1-beta) g, Nesterov u = (1-beta) g + beta m
  *  ([P2] change 2); HEAVY_BALL: m <- beta m + g, Nesterov u = g + beta m
  *  ([P4] Muon source). ns_precision BF16: bf16 MFMA operands with fp32
- *  accumulation; FP32: fp32 throughout (debug / reference mode). */
+ *  accumulation; FP32: fp32 throughout (debug / reference mode).
+ *  stream_groups (not a method parameter; default 2): 2 lets muon_step split
+ *  the tiled matrices (4 or more) into two cost-balanced groups whose
+ *  Newton–Schulz launches run on the caller's stream and on a second,
+ *  default-priority stream the handle owns, forked after the momentum kernel
+ *  and joined before the parameter update, so one group's kernels fill the
+ *  other's tails; 1 keeps every launch on the caller's stream. Results are
+ *  bit-identical either way. */
 typedef struct muon_hparams {
     float momentum;
     int32_t nesterov;
@@ -92,6 +99,7 @@ typedef struct muon_hparams {
     float normuon_beta2;
     float normuon_eps;
     float weight_decay;
+    int32_t stream_groups;
 } muon_hparams;
 
 /* Opaque handle: the host-side plan for one table on one device. */

@@ -75,6 +75,7 @@ class muon_hparams(ctypes.Structure):
         ("normuon_beta2", ctypes.c_float),
         ("normuon_eps", ctypes.c_float),
         ("weight_decay", ctypes.c_float),
+        ("stream_groups", ctypes.c_int32),
     ]
 
 
@@ -254,7 +255,7 @@ def check(status: int, h=None, what: str = "") -> None:
 
 def make_hparams(momentum=0.95, nesterov=1, momentum_kind=MUON_MOMENTUM_LERP, ns_steps=5, coeffs=None,
                  ns_eps=1e-7, precision="bf16", normuon=0, normuon_beta2=0.95, normuon_eps=1e-10,
-                 weight_decay=0.0) -> muon_hparams:
+                 weight_decay=0.0, stream_groups=2) -> muon_hparams:
     hp = muon_hparams_default()
     hp.momentum = momentum
     hp.nesterov = nesterov
@@ -269,6 +270,7 @@ def make_hparams(momentum=0.95, nesterov=1, momentum_kind=MUON_MOMENTUM_LERP, ns
     hp.normuon_beta2 = normuon_beta2
     hp.normuon_eps = normuon_eps
     hp.weight_decay = weight_decay
+    hp.stream_groups = stream_groups
     return hp
 
 

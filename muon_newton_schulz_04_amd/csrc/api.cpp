@@ -33,7 +33,14 @@ struct muon_handle {
     bool profiling = false;
     std::vector<Rec> recs;          // recorded, not yet read
     std::vector<hipEvent_t> spare;  // events for reuse
+    // second stream group: its own stream (default priority, non-blocking)
+    // and the fork / join events that order it against the caller's stream
+    hipStream_t aux = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     ~muon_handle() {
+        if (ev_fork) (void)hipEventDestroy(ev_fork);
+        if (ev_join) (void)hipEventDestroy(ev_join);
+        if (aux) (void)hipStreamDestroy(aux);
         for (auto& r : recs) {
             (void)hipEventDestroy(r.start);
             (void)hipEventDestroy(r.stop);
@@ -213,6 +220,9 @@ muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, co
         if (e == hipSuccess) e = up(L.off_poly, L.poly.data(), L.poly.size() * sizeof(muon::TileWork));
         if (e == hipSuccess) e = up(L.off_update, L.update.data(), L.update.size() * sizeof(muon::TileWork));
     }
+    if (e == hipSuccess && P.n_groups > 1) e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
+    if (e == hipSuccess && P.n_groups > 1) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess && P.n_groups > 1) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
     if (e == hipSuccess && P.rows_total) e = hipMemset(h->ws + P.off_v, 0, (size_t)P.rows_total * 4);
     if (e == hipSuccess && P.mats.size()) e = hipMemset(h->ws + P.off_status, 0, P.mats.size() * 4);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -254,24 +264,25 @@ muon_status muon_step(muon_handle* h, float* params, const float* grads, float* 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const muon::LaunchCtx L = make_ctx(h, st);
     hipError_t e = hipSuccess;
-    // run one launch, bracketed by events when profiling
-    auto run = [&](int kind, const char* what, auto&& launch) -> muon_status {
+    // run one launch on stream `on`, bracketed by events when profiling
+    auto run_on = [&](hipStream_t on, int kind, const char* what, auto&& launch) -> muon_status {
         hipEvent_t a = nullptr, b = nullptr;
         if (h->profiling) {
             hipError_t pe = take_event(h, &a);
             if (pe == hipSuccess) pe = take_event(h, &b);
-            if (pe == hipSuccess) pe = hipEventRecord(a, st);
+            if (pe == hipSuccess) pe = hipEventRecord(a, on);
             if (pe != hipSuccess) return hip_fail(h, pe, "profiling event");
         }
         hipError_t le = launch();
         if (le != hipSuccess) return hip_fail(h, le, what);
         if (h->profiling) {
-            hipError_t pe = hipEventRecord(b, st);
+            hipError_t pe = hipEventRecord(b, on);
             if (pe != hipSuccess) return hip_fail(h, pe, "profiling event");
             h->recs.push_back({kind, a, b});
         }
         return MUON_OK;
     };
+    auto run = [&](int kind, const char* what, auto&& launch) { return run_on(st, kind, what, launch); };
     s = run(MUON_KERNEL_MOMENTUM, "momentum kernel", [&] {
         return muon::launch_momentum(L, grads, momentum, beta, P.hp.nesterov,
                                      P.hp.momentum_kind == MUON_MOMENTUM_HEAVY_BALL);
@@ -290,26 +301,48 @@ muon_status muon_step(muon_handle* h, float* params, const float* grads, float* 
         });
         if (s != MUON_OK) return s;
     }
-    for (int k = 0; k < steps; ++k) {
-        void* xin = k == 0 ? L.xt : ((k & 1) ? L.x1 : L.x0);
-        void* xout = k == 0 ? L.x1 : ((k & 1) ? L.x0 : L.x1);
-        const float ca = P.hp.ns_coeffs[k][0], cb = P.hp.ns_coeffs[k][1], cc = P.hp.ns_coeffs[k][2];
-        const int first = k == 0;
-        const int rowstats = (k == steps - 1) && P.hp.normuon;
-        for (const auto& T : P.lists) {
-            const muon::GemmList G = make_list(h, T);
-            const bool big = !L.fp32 && G.T >= 128;
-            auto stage = [&](int mode, const void* x, const void* a, void* o, int rs) {
-                return big ? muon::launch_ns_stage_big(L, G, mode, x, a, o, ca, cb, cc, first, P.hp.ns_eps, rs)
-                           : muon::launch_ns_stage(L, G, mode, x, a, o, ca, cb, cc, first, P.hp.ns_eps, rs);
-            };
-            s = run(MUON_KERNEL_GRAM, "Gram kernel", [&] { return stage(muon::NS_GRAM, xin, nullptr, L.a, 0); });
-            if (s != MUON_OK) return s;
-            s = run(MUON_KERNEL_POLY, "polynomial kernel", [&] { return stage(muon::NS_POLY, nullptr, L.a, L.b, 0); });
-            if (s != MUON_OK) return s;
-            s = run(MUON_KERNEL_UPDATE, "update kernel", [&] { return stage(muon::NS_UPDATE, xin, L.b, xout, rowstats); });
-            if (s != MUON_OK) return s;
+    // tiled Newton–Schulz: group 0 on the caller's stream, group 1 (if any)
+    // on the handle's second stream, forked after the momentum kernel and
+    // joined before NorMuon / apply
+    if (P.n_groups > 1) {
+        e = hipEventRecord(h->ev_fork, st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(h->aux, h->ev_fork, 0);
+        if (e != hipSuccess) return hip_fail(h, e, "stream fork");
+    }
+    for (int grp = 0; grp < P.n_groups; ++grp) {
+        const hipStream_t sg = grp == 0 ? st : h->aux;
+        muon::LaunchCtx Lg = L;
+        Lg.stream = sg;
+        for (int k = 0; k < steps; ++k) {
+            void* xin = k == 0 ? L.xt : ((k & 1) ? L.x1 : L.x0);
+            void* xout = k == 0 ? L.x1 : ((k & 1) ? L.x0 : L.x1);
+            const float ca = P.hp.ns_coeffs[k][0], cb = P.hp.ns_coeffs[k][1], cc = P.hp.ns_coeffs[k][2];
+            const int first = k == 0;
+            const int rowstats = (k == steps - 1) && P.hp.normuon;
+            for (const auto& T : P.lists) {
+                if (T.group != grp) continue;
+                const muon::GemmList G = make_list(h, T);
+                const bool big = !L.fp32 && G.T >= 128;
+                auto stage = [&](int mode, const void* x, const void* a, void* o, int rs) {
+                    return big ? muon::launch_ns_stage_big(Lg, G, mode, x, a, o, ca, cb, cc, first, P.hp.ns_eps, rs)
+                               : muon::launch_ns_stage(Lg, G, mode, x, a, o, ca, cb, cc, first, P.hp.ns_eps, rs);
+                };
+                s = run_on(sg, MUON_KERNEL_GRAM, "Gram kernel",
+                           [&] { return stage(muon::NS_GRAM, xin, nullptr, L.a, 0); });
+                if (s != MUON_OK) return s;
+                s = run_on(sg, MUON_KERNEL_POLY, "polynomial kernel",
+                           [&] { return stage(muon::NS_POLY, nullptr, L.a, L.b, 0); });
+                if (s != MUON_OK) return s;
+                s = run_on(sg, MUON_KERNEL_UPDATE, "update kernel",
+                           [&] { return stage(muon::NS_UPDATE, xin, L.b, xout, rowstats); });
+                if (s != MUON_OK) return s;
+            }
         }
+    }
+    if (P.n_groups > 1) {
+        e = hipEventRecord(h->ev_join, h->aux);
+        if (e == hipSuccess) e = hipStreamWaitEvent(st, h->ev_join, 0);
+        if (e != hipSuccess) return hip_fail(h, e, "stream join");
     }
     const float* f = nullptr;
     if (P.hp.normuon) {

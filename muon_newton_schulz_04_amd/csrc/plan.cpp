@@ -55,6 +55,7 @@ muon_status check_hparams(const muon_hparams* hp, std::string* err) {
         return bad("normuon_beta2 must be in [0, 1]");
     if (!finite(hp->normuon_eps) || hp->normuon_eps < 0.f) return bad("normuon_eps must be finite and >= 0");
     if (!finite(hp->weight_decay)) return bad("weight_decay must be finite");
+    if (hp->stream_groups != 1 && hp->stream_groups != 2) return bad("stream_groups must be 1 or 2");
     return MUON_OK;
 }
 
@@ -224,7 +225,33 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
     for (int32_t mi : P.active)
         for (int t = 0; t < P.mats[mi].ew_count; ++t) P.ew_map.push_back(mi);
 
-    // ---- GEMM work lists per tile size ----
+    // ---- stream groups: longest-processing-time split of the tiled matrices ----
+    std::vector<int> group_of(P.mats.size(), 0);
+    {
+        std::vector<std::pair<double, int32_t>> cost;
+        for (int32_t mi : P.active) {
+            const MatDesc& d = P.mats[mi];
+            if (P.is_small(d)) continue;
+            const double m = d.m, nn = d.n;
+            cost.push_back({m * (m + 1) * nn + m * (m + 1) * m + 2 * m * m * nn, mi});
+        }
+        if (P.hp.stream_groups > 1 && cost.size() >= (size_t)kMinSplit) {
+            P.n_groups = 2;
+            std::stable_sort(cost.begin(), cost.end(),
+                             [](const std::pair<double, int32_t>& a, const std::pair<double, int32_t>& b) {
+                                 return a.first > b.first;
+                             });
+            double load[2] = {0.0, 0.0};
+            for (const auto& c : cost) {
+                const int g = load[0] <= load[1] ? 0 : 1;
+                group_of[c.second] = g;
+                load[g] += c.first;
+            }
+        }
+    }
+
+    // ---- GEMM work lists per (group, tile size) ----
+    for (int grp = 0; grp < P.n_groups; ++grp)
     for (int T : {256, 128, 64}) {
         std::vector<std::vector<TileWork>> g, u;
         std::vector<double> cg, cp, cu;
@@ -232,10 +259,13 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
             const MatDesc& d = P.mats[mi];
             if (d.T != T) continue;
             if (P.is_small(d)) {
-                P.small.push_back(mi);
-                P.small_np = std::max(P.small_np, d.n_pad);
+                if (grp == 0) {
+                    P.small.push_back(mi);
+                    P.small_np = std::max(P.small_np, d.n_pad);
+                }
                 continue;
             }
+            if (group_of[mi] != grp) continue;
             const int tm = d.m_pad / T, tn = d.n_pad / T;
             std::vector<TileWork> gl, ul;
             for (int ti = 0; ti < tm; ++ti)
@@ -251,6 +281,7 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
         if (g.empty()) continue;  // (also when every matrix of this size is small)
         TileList L;
         L.T = T;
+        L.group = grp;
         L.gram = order_for_xcds(g, cg);
         L.poly = order_for_xcds(g, cp);
         L.update = order_for_xcds(u, cu);
@@ -311,4 +342,5 @@ extern "C" void muon_hparams_default(muon_hparams* hp) {
     hp->normuon_beta2 = 0.95f;
     hp->normuon_eps = 1e-10f;
     hp->weight_decay = 0.0f;
+    hp->stream_groups = 2;
 }

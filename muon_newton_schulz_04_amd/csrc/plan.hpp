@@ -14,8 +14,13 @@
 
 namespace muon {
 
+// Tiled matrices needed before the Newton–Schulz launches are split over two
+// streams (fewer gain nothing from the overlap).
+constexpr int kMinSplit = 4;
+
 struct TileList {
     int T = 0;
+    int group = 0;                      // stream group (see Plan::n_groups)
     std::vector<TileWork> gram, poly, update;
     size_t off_gram = 0, off_poly = 0, off_update = 0;  // workspace byte offsets
 };
@@ -27,7 +32,11 @@ struct Plan {
     std::vector<uint8_t> active_flag;   // !frozen
     std::vector<int32_t> active;        // active matrix indices
     std::vector<int32_t> ew_map;        // elementwise tile -> matrix
-    std::vector<TileList> lists;        // one per tile size in use
+    std::vector<TileList> lists;        // one per (stream group, tile size) in use
+    // The tiled matrices are split into n_groups cost-balanced groups whose
+    // Newton–Schulz launches go to separate streams, so that one group's
+    // kernels fill the other's tails and launch gaps.
+    int n_groups = 1;
     std::vector<int32_t> small;         // active matrices of the one-workgroup Newton–Schulz
     int small_np = 0;                   // their largest n_pad
     size_t off_small = 0;

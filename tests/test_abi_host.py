@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_struct_sizes_match_c_layout():
     assert ctypes.sizeof(B.muon_matrix) == 48
-    assert ctypes.sizeof(B.muon_hparams) == 4 * 4 + 16 * 3 * 4 + 4 * 6
+    assert ctypes.sizeof(B.muon_hparams) == 4 * 4 + 16 * 3 * 4 + 4 * 7
     assert ctypes.sizeof(B.muon_layout) == 8 + 8 + 8 * 4 + 8
 
 
@@ -50,6 +50,7 @@ def test_hparams_default_values():
         assert (round(a, 4), round(b, 4), round(c, 4)) == (3.4445, -4.775, 2.0315)
     assert math.isclose(hp.ns_eps, 1e-7, rel_tol=1e-6)
     assert hp.normuon == 0 and math.isclose(hp.normuon_eps, 1e-10, rel_tol=1e-6)
+    assert hp.stream_groups == 2
 
 
 def _ws(entries, hp=None):
@@ -92,6 +93,9 @@ def test_validation_errors():
     assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0)], bad)[0] == B.MUON_E_INVALID_ARG
     bad = B.muon_hparams_default()
     bad.ns_precision = 3
+    assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0)], bad)[0] == B.MUON_E_INVALID_ARG
+    bad = B.muon_hparams_default()
+    bad.stream_groups = 3
     assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0)], bad)[0] == B.MUON_E_INVALID_ARG
     # adjacent (touching) entries are fine; empty table is fine
     assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0), M(4, 4, 1, 16, 1.0, 1.0, 0, 0)], hp)[0] == B.MUON_OK

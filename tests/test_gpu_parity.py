@@ -98,6 +98,50 @@ LARGE_TILES = [
 ]
 
 
+def test_stream_groups_give_identical_results():
+    # the tiled matrices split over two streams (default) or all on the
+    # caller's stream: the same kernels on the same tiles, so bit-identical
+    w = custom_workload(110, LARGE_TILES + [(200, 300, 2, "spike"), (64, 64, 3, "rank8")], steps=2, lr=0.05,
+                        weight_decay=0.1, normuon=1)
+    runs = [GpuRun(w, stream_groups=g) for g in (1, 2)]
+    for t in range(2):
+        for r in runs:
+            r.load_grads(t)
+            r.step()
+        for name in ("params", "mom"):
+            a, b = getattr(runs[0], name), getattr(runs[1], name)
+            assert torch.equal(a, b), f"step {t}: {name} differs between one and two stream groups"
+        assert torch.equal(runs[0].H.view(B.MUON_VIEW_NS_OUT, torch.bfloat16),
+                           runs[1].H.view(B.MUON_VIEW_NS_OUT, torch.bfloat16))
+
+
+def test_step_captured_in_a_hip_graph_replays_like_eager():
+    # muon_step allocates nothing, never synchronises and records no memset,
+    # and its two-stream fork / join is event-based, so a caller can capture it
+    # in a HIP graph; every replay must equal the eager step on the same state
+    w = custom_workload(111, LARGE_TILES + [(64, 64, 3, "rank8")], steps=1, lr=0.05, weight_decay=0.1)
+    run = GpuRun(w)
+    run.load_grads(0)
+    run.step()  # past the first-step paths
+    eager_p, eager_m = run.params.clone(), run.mom.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        run.H.step(run.params, run.grads, run.mom, w.lr)
+    torch.cuda.synchronize()
+    # capture does not execute: restart both copies from the same state
+    run.params.copy_(eager_p)
+    run.mom.copy_(eager_m)
+    for r in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        run.H.step(eager_p, run.grads, eager_m, w.lr)  # eager, same handle, other buffers
+        torch.cuda.synchronize()
+        assert torch.equal(run.params, eager_p), f"replay {r}: params differ from the eager step"
+        assert torch.equal(run.mom, eager_m), f"replay {r}: momentum differs from the eager step"
+
+
 def test_weight_decay_large_tiles_ragged():
     w = custom_workload(109, LARGE_TILES, steps=3, lr=0.05, weight_decay=0.1)
     _run_all_stages(w, 3)
