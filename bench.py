@@ -110,17 +110,21 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str) -> dict:
             else:
                 unmatched.add(name[:80])
                 continue
-            vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
-        per[counter] = {k: statistics.median(v) for k, v in vals.items()}
+            grid = int(r["Grid_Size"])
+            vals.setdefault(key, {}).setdefault(grid, []).append(float(r["Counter_Value"]) * 1024.0)
+        # per kernel class, the launches with the largest grid: the kernel
+        # pass's one-stream launches, which the roofline is measured on
+        per[counter] = {k: statistics.median(v[max(v)]) for k, v in vals.items()}
     fscale = COPY_BYTES / per["FETCH_SIZE"]["copy"]
     wscale = COPY_BYTES / per["WRITE_SIZE"]["copy"]
     cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc {c} -f csv -d $REPO/gpurun_out/{d} "
-           "-o run -- python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-events --copy-calibration")
+           "-o run -- python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
     out = {"workload": workload, "source_hash": _kernel_source_hash(),
            "commands": [cmd.format(c="FETCH_SIZE", d="pmc_fetch"), cmd.format(c="WRITE_SIZE", d="pmc_write"),
                         "python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write"],
            "note": "FETCH_SIZE/WRITE_SIZE are KiB per dispatch; each is scaled so that the 1 GiB calibration "
-                   "read/write (torch.neg over 2^28 floats) counts 2^30 bytes; medians over dispatches",
+                   "read/write (torch.neg over 2^28 floats) counts 2^30 bytes; medians over the dispatches with "
+                   "the largest grid of each kernel class (the one-stream kernel pass the roofline is timed on)",
            "copy_fetch_bytes": per["FETCH_SIZE"]["copy"], "copy_write_bytes": per["WRITE_SIZE"]["copy"],
            "fetch_scale": fscale, "write_scale": wscale, "kernels": {}}
     for k in per["FETCH_SIZE"]:
@@ -132,6 +136,55 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str) -> dict:
     if unmatched:
         print("unmatched kernels:", sorted(unmatched), file=sys.stderr)
     return out
+
+
+def _short_kernel(name: str) -> str:
+    """A readable label for a libmuon kernel from its demangled name."""
+    import re
+    mode = {"0": "GRAM", "1": "POLY", "2": "UPDATE"}
+    m = re.search(r"k_ns_big<(\d+), (\d+), (\d), (\w+)>", name)
+    if m:
+        return (f"k_ns_big {mode[m.group(3)]} T={m.group(1)} waves={2 * int(m.group(2))}"
+                + (" +rowstats" if m.group(4) == "true" else ""))
+    m = re.search(r"k_ns<([^,]+), (\d+), (\d)>", name)
+    if m:
+        return f"k_ns<{'bf16' if 'bf' in m.group(1) else 'f32'}> {mode[m.group(3)]} T={m.group(2)}"
+    for k in ("k_ns_small", "k_momentum", "k_apply", "k_normuon", "k_zero_momentum", "k_fill_zero"):
+        if k in name:
+            return k
+    return name[:60]
+
+
+def trace_summary(trace_dir: str, workload: str, command: str) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace run: per kernel and grid
+    size (the two-stream launches of a stage have smaller grids than the
+    one-stream launches of the kernel pass), calls and durations."""
+    import csv
+    import glob
+    import statistics
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    rows = {}
+    total = 0.0
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(wg, 1)
+            rows.setdefault((_short_kernel(r["Kernel_Name"]), grid), []).append(dur)
+            total += dur
+    out = [f"# rocprofv3 kernel trace — Muon step, {workload}", "",
+           "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
+           f"Kernel sources hash (bench.py `source_hash`): `{_kernel_source_hash()}`. The bench runs the timed steps "
+           "with the shipped two-stream schedule (a stage's launches split over two streams, smaller grids), then "
+           "the kernel pass with every launch on one stream (full grids); the roofline uses the full-grid rows.", "",
+           "| kernel | workgroups | calls | avg µs | median µs | min µs | max µs | share |",
+           "|---|---|---|---|---|---|---|---|"]
+    for (k, grid), d in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| {k} | {grid} | {len(d)} | {statistics.mean(d):.1f} | {statistics.median(d):.1f} | "
+                   f"{min(d):.1f} | {max(d):.1f} | {100 * sum(d) / total:.1f}% |")
+    return "\n".join(out) + "\n"
 
 
 def cpu_baseline(seconds: float) -> dict:
@@ -184,10 +237,21 @@ def main() -> int:
     ap.add_argument("--no-events", action="store_true", help="do not time kernels with events")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB once per pass (HBM counter calibration)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
+                    help="summarise a rocprofv3 --kernel-trace run into profiles/kernel_stats_<workload>.md and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into "
                          "profiles/traffic_<workload>.json and exit")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        from workloads import get_workload as _gw
+        wname = _gw(args.config).name
+        md = trace_summary(args.trace_summary[0], wname, args.trace_summary[1])
+        with open(os.path.join(ROOT, "profiles", f"kernel_stats_{wname}.md"), "w") as f:
+            f.write(md)
+        print(md)
+        return 0
 
     if args.pmc_summary:
         from workloads import get_workload as _gw
