@@ -75,6 +75,7 @@ muon::LaunchCtx make_ctx(const muon_handle* h, hipStream_t stream) {
     L.mats = reinterpret_cast<const muon::MatDesc*>(ws + P.off_mats);
     L.ew_map = reinterpret_cast<const int32_t*>(ws + P.off_ewmap);
     L.active = reinterpret_cast<const int32_t*>(ws + P.off_active);
+    L.ew_tile0 = 0;
     L.ew_tiles = (int)P.ew_map.size();
     L.n_active = (int)P.active.size();
     L.xt = ws + P.off_xt;
@@ -282,37 +283,43 @@ muon_status muon_step(muon_handle* h, float* params, const float* grads, float* 
         }
         return MUON_OK;
     };
-    auto run = [&](int kind, const char* what, auto&& launch) { return run_on(st, kind, what, launch); };
-    s = run(MUON_KERNEL_MOMENTUM, "momentum kernel", [&] {
-        return muon::launch_momentum(L, grads, momentum, beta, P.hp.nesterov,
-                                     P.hp.momentum_kind == MUON_MOMENTUM_HEAVY_BALL);
-    });
-    if (s != MUON_OK) return s;
-
     const int steps = P.hp.ns_steps;
-    if (!P.small.empty()) {
-        muon::NsCoeffs co{};
-        std::memcpy(co.c, P.hp.ns_coeffs, sizeof(co.c));
-        co.steps = steps;
-        co.eps = P.hp.ns_eps;
-        s = run(MUON_KERNEL_NS_SMALL, "small-matrix Newton-Schulz kernel", [&] {
-            return muon::launch_ns_small(L, reinterpret_cast<const int32_t*>(h->ws + P.off_small), (int)P.small.size(),
-                                         P.small_np, co, ns_out(h), P.hp.normuon);
-        });
-        if (s != MUON_OK) return s;
-    }
-    // tiled Newton–Schulz: group 0 on the caller's stream, group 1 (if any)
-    // on the handle's second stream, forked after the momentum kernel and
-    // joined before NorMuon / apply
-    if (P.n_groups > 1) {
-        e = hipEventRecord(h->ev_fork, st);
-        if (e == hipSuccess) e = hipStreamWaitEvent(h->aux, h->ev_fork, 0);
-        if (e != hipSuccess) return hip_fail(h, e, "stream fork");
-    }
+    // Each stream group runs its whole chain: momentum of its matrices (and,
+    // in group 0, the small-matrix Newton–Schulz), its tiled Newton–Schulz
+    // launches, NorMuon and the parameter update. Group 0 runs on the
+    // caller's stream; group 1 runs on the handle's second stream, forked
+    // after group 0's momentum kernel and joined at the end. The stagger puts
+    // group 1's momentum under group 0's first GEMMs and group 0's update of
+    // the parameters under group 1's last GEMMs.
     for (int grp = 0; grp < P.n_groups; ++grp) {
         const hipStream_t sg = grp == 0 ? st : h->aux;
         muon::LaunchCtx Lg = L;
         Lg.stream = sg;
+        Lg.ew_tile0 = P.ew_begin[grp];
+        Lg.ew_tiles = P.ew_begin[grp + 1] - P.ew_begin[grp];
+        Lg.active = L.active + P.act_begin[grp];
+        Lg.n_active = P.act_begin[grp + 1] - P.act_begin[grp];
+        s = run_on(sg, MUON_KERNEL_MOMENTUM, "momentum kernel", [&] {
+            return muon::launch_momentum(Lg, grads, momentum, beta, P.hp.nesterov,
+                                         P.hp.momentum_kind == MUON_MOMENTUM_HEAVY_BALL);
+        });
+        if (s != MUON_OK) return s;
+        if (grp == 0 && P.n_groups > 1) {
+            e = hipEventRecord(h->ev_fork, st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(h->aux, h->ev_fork, 0);
+            if (e != hipSuccess) return hip_fail(h, e, "stream fork");
+        }
+        if (grp == 0 && !P.small.empty()) {
+            muon::NsCoeffs co{};
+            std::memcpy(co.c, P.hp.ns_coeffs, sizeof(co.c));
+            co.steps = steps;
+            co.eps = P.hp.ns_eps;
+            s = run_on(sg, MUON_KERNEL_NS_SMALL, "small-matrix Newton-Schulz kernel", [&] {
+                return muon::launch_ns_small(Lg, reinterpret_cast<const int32_t*>(h->ws + P.off_small),
+                                             (int)P.small.size(), P.small_np, co, ns_out(h), P.hp.normuon);
+            });
+            if (s != MUON_OK) return s;
+        }
         for (int k = 0; k < steps; ++k) {
             void* xin = k == 0 ? L.xt : ((k & 1) ? L.x1 : L.x0);
             void* xout = k == 0 ? L.x1 : ((k & 1) ? L.x0 : L.x1);
@@ -338,23 +345,23 @@ muon_status muon_step(muon_handle* h, float* params, const float* grads, float* 
                 if (s != MUON_OK) return s;
             }
         }
+        const float* f = nullptr;
+        if (P.hp.normuon) {
+            s = run_on(sg, MUON_KERNEL_NORMUON, "NorMuon kernel",
+                       [&] { return muon::launch_normuon(Lg, P.hp.normuon_beta2, P.hp.normuon_eps); });
+            if (s != MUON_OK) return s;
+            f = L.f;
+        }
+        s = run_on(sg, MUON_KERNEL_APPLY, "apply kernel",
+                   [&] { return muon::launch_apply(Lg, ns_out(h), f, params, lr, P.hp.weight_decay); });
+        if (s != MUON_OK) return s;
     }
     if (P.n_groups > 1) {
         e = hipEventRecord(h->ev_join, h->aux);
         if (e == hipSuccess) e = hipStreamWaitEvent(st, h->ev_join, 0);
         if (e != hipSuccess) return hip_fail(h, e, "stream join");
     }
-    const float* f = nullptr;
-    if (P.hp.normuon) {
-        s = run(MUON_KERNEL_NORMUON, "NorMuon kernel",
-                [&] { return muon::launch_normuon(L, P.hp.normuon_beta2, P.hp.normuon_eps); });
-        if (s != MUON_OK) return s;
-        f = L.f;
-    }
-    s = run(MUON_KERNEL_APPLY, "apply kernel",
-            [&] { return muon::launch_apply(L, ns_out(h), f, params, lr, P.hp.weight_decay); });
-    (void)e;
-    return s;
+    return MUON_OK;
 }
 
 muon_status muon_reset(muon_handle* h, float* momentum, int64_t numel, void* stream) {
@@ -459,13 +466,13 @@ muon_status muon_work_stats(const muon_handle* h, muon_work* out) {
     if (P.hp.normuon) out->bytes[MUON_KERNEL_NORMUON] = 4.0 * (rowpart + 3.0 * rows);
     const int64_t nl = (int64_t)P.lists.size();
     const int64_t any = P.active.empty() ? 0 : 1;
-    out->launches[MUON_KERNEL_MOMENTUM] = any;
+    out->launches[MUON_KERNEL_MOMENTUM] = any * P.n_groups;
     out->launches[MUON_KERNEL_GRAM] = steps * nl;
     out->launches[MUON_KERNEL_POLY] = steps * nl;
     out->launches[MUON_KERNEL_UPDATE] = steps * nl;
     out->launches[MUON_KERNEL_NS_SMALL] = P.small.empty() ? 0 : 1;
-    out->launches[MUON_KERNEL_NORMUON] = P.hp.normuon ? any : 0;
-    out->launches[MUON_KERNEL_APPLY] = any;
+    out->launches[MUON_KERNEL_NORMUON] = P.hp.normuon ? any * P.n_groups : 0;
+    out->launches[MUON_KERNEL_APPLY] = any * P.n_groups;
     return MUON_OK;
 }
 

@@ -111,10 +111,10 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MatDesc* __restrict
                                                        const int32_t* __restrict__ ew_map,
                                                        const float* __restrict__ grads,
                                                        float* __restrict__ mom, XT* __restrict__ xt,
-                                                       float* __restrict__ partials, MomParams P) {
+                                                       float* __restrict__ partials, MomParams P, int tile0) {
     __shared__ float lds[TS][TS + 1];
     __shared__ float red[4];
-    const int tile = blockIdx.x;
+    const int tile = tile0 + blockIdx.x;
     const int mi = ew_map[tile];
     const MatDesc d = mats[mi];
     const TileCoord tc = decode_tile(d, tile, mi);
@@ -214,9 +214,9 @@ template <typename XT>
 __global__ __launch_bounds__(kThreads) void k_apply(const MatDesc* __restrict__ mats,
                                                     const int32_t* __restrict__ ew_map,
                                                     const XT* __restrict__ xo, const float* __restrict__ fr,
-                                                    float* __restrict__ params, float lr, float wd) {
+                                                    float* __restrict__ params, float lr, float wd, int tile0) {
     __shared__ float lds[TS][TS + 1];
-    const int tile = blockIdx.x;
+    const int tile = tile0 + blockIdx.x;
     const int mi = ew_map[tile];
     const MatDesc d = mats[mi];
     const TileCoord tc = decode_tile(d, tile, mi);
@@ -376,10 +376,10 @@ hipError_t launch_momentum(const LaunchCtx& L, const float* grads, float* mom, f
     MomParams P{beta, nesterov, heavy};
     if (L.fp32)
         k_momentum<float><<<L.ew_tiles, kThreads, 0, L.stream>>>(L.mats, L.ew_map, grads, mom,
-                                                                 (float*)L.xt, L.partials, P);
+                                                                 (float*)L.xt, L.partials, P, L.ew_tile0);
     else
         k_momentum<bf16><<<L.ew_tiles, kThreads, 0, L.stream>>>(L.mats, L.ew_map, grads, mom, (bf16*)L.xt,
-                                                                L.partials, P);
+                                                                L.partials, P, L.ew_tile0);
     return hipGetLastError();
 }
 
@@ -387,9 +387,10 @@ hipError_t launch_apply(const LaunchCtx& L, const void* xo, const float* f, floa
     if (L.ew_tiles == 0) return hipSuccess;
     if (L.fp32)
         k_apply<float><<<L.ew_tiles, kThreads, 0, L.stream>>>(L.mats, L.ew_map, (const float*)xo, f, params, lr,
-                                                              wd);
+                                                              wd, L.ew_tile0);
     else
-        k_apply<bf16><<<L.ew_tiles, kThreads, 0, L.stream>>>(L.mats, L.ew_map, (const bf16*)xo, f, params, lr, wd);
+        k_apply<bf16><<<L.ew_tiles, kThreads, 0, L.stream>>>(L.mats, L.ew_map, (const bf16*)xo, f, params, lr, wd,
+                                                             L.ew_tile0);
     return hipGetLastError();
 }
 

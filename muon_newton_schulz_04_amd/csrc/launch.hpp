@@ -15,8 +15,9 @@ struct LaunchCtx {
     const MatDesc* mats;
     const int32_t* ew_map;    // elementwise tile -> matrix
     const int32_t* active;    // active matrix indices
-    int ew_tiles;
-    int n_active;
+    int ew_tile0;             // first elementwise tile of this launch (a stream group's range)
+    int ew_tiles;             // elementwise tiles of this launch
+    int n_active;             // active matrices from `active` on
     void* xt;                 // momentum output X~ (canonical, padded)
     void* x0;                 // ping-pong X buffers
     void* x1;

@@ -221,21 +221,20 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
         *err = "table too large";
         return MUON_E_SHAPE;
     }
-    P.ew_map.reserve((size_t)ew_tiles);
-    for (int32_t mi : P.active)
-        for (int t = 0; t < P.mats[mi].ew_count; ++t) P.ew_map.push_back(mi);
 
     // ---- stream groups: longest-processing-time split of the tiled matrices ----
     std::vector<int> group_of(P.mats.size(), 0);
     {
         std::vector<std::pair<double, int32_t>> cost;
+        int64_t tiles64 = 0;  // update output in 64 x 64 tiles
         for (int32_t mi : P.active) {
             const MatDesc& d = P.mats[mi];
             if (P.is_small(d)) continue;
             const double m = d.m, nn = d.n;
             cost.push_back({m * (m + 1) * nn + m * (m + 1) * m + 2 * m * m * nn, mi});
+            tiles64 += (int64_t)(d.m_pad / 64) * (d.n_pad / 64);
         }
-        if (P.hp.stream_groups > 1 && cost.size() >= (size_t)kMinSplit) {
+        if (P.hp.stream_groups > 1 && cost.size() >= (size_t)kMinSplit && tiles64 <= kMaxSplitTiles64) {
             P.n_groups = 2;
             std::stable_sort(cost.begin(), cost.end(),
                              [](const std::pair<double, int32_t>& a, const std::pair<double, int32_t>& b) {
@@ -248,6 +247,27 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
                 load[g] += c.first;
             }
         }
+    }
+
+    // ---- order the active matrices and their elementwise tiles by group ----
+    {
+        std::vector<int32_t> ordered;
+        for (int grp = 0; grp < P.n_groups; ++grp) {
+            P.act_begin[grp] = (int)ordered.size();
+            for (int32_t mi : P.active)
+                if (group_of[mi] == grp) ordered.push_back(mi);
+        }
+        P.act_begin[P.n_groups] = (int)ordered.size();
+        P.active = ordered;
+        P.ew_map.reserve((size_t)ew_tiles);
+        int g = 0;
+        for (size_t k = 0; k < P.active.size(); ++k) {
+            while (g < P.n_groups && (int)k == P.act_begin[g]) P.ew_begin[g++] = (int)P.ew_map.size();
+            MatDesc& d = P.mats[P.active[k]];
+            d.ew_start = (int32_t)P.ew_map.size();
+            for (int t = 0; t < d.ew_count; ++t) P.ew_map.push_back(P.active[k]);
+        }
+        while (g <= P.n_groups) P.ew_begin[g++] = (int)P.ew_map.size();
     }
 
     // ---- GEMM work lists per (group, tile size) ----
