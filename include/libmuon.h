@@ -189,6 +189,27 @@ enum {
  * stream work of the last muon_step has completed. */
 muon_status muon_debug_view(const muon_handle* h, int32_t which, void** dev_ptr, size_t* bytes);
 
+/* ---- host-side schedules (scalars for muon_step's lr and momentum_coef) ---
+ * Pure host functions; no handle, no device. Out-of-range arguments give NaN. */
+
+/* Warmup-stable-decay LR multiplier ([P4] hyper-parameter section, and the
+ * [P3] FlexAttention record's schedule): for step it in [0, num_iterations),
+ * (it + 1) / warmup_iters while it < warmup_iters, then 1, and from
+ * num_iterations - warmdown_iters on (num_iterations - it) / warmdown_iters,
+ * i.e. linear to 0 at the end. The Muon group uses warmup_iters = 0. */
+float muon_lr_wsd(int64_t it, int64_t num_iterations, int64_t warmup_iters, int64_t warmdown_iters);
+
+/* Cool-down-to-floor LR multiplier ([P2] change 3, reading stated in the
+ * design notes): with x = min(step / main_iterations, 1), the multiplier is
+ * floor + (1 - floor) * min(1, (1 - x) / cooldown_frac): 1 until the last
+ * cooldown_frac of the main phase, then linear down to floor, and flat at
+ * floor for every extension step past main_iterations ([P2]: 0.80, 0.30). */
+float muon_lr_cooldown_floor(int64_t step, int64_t main_iterations, float cooldown_frac, float floor);
+
+/* Momentum warm-up ([P3] training loop): frac = min(step / warmup_steps, 1),
+ * momentum = (1 - frac) start + frac end ([P3]: 500 steps, 0.85 -> 0.95). */
+float muon_momentum_warmup(int64_t step, int64_t warmup_steps, float start, float end);
+
 /* ---- measurement (benchmarks) ------------------------------------------- */
 
 enum {

@@ -123,6 +123,9 @@ _SIGS = {
     "muon_profile_enable": (ctypes.c_int, [_P, ctypes.c_int32]),
     "muon_profile_read": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                          ctypes.POINTER(ctypes.c_double)]),
+    "muon_lr_wsd": (ctypes.c_float, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
+    "muon_lr_cooldown_floor": (ctypes.c_float, [ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_float]),
+    "muon_momentum_warmup": (ctypes.c_float, [ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_float]),
 }
 
 _lib = None
@@ -161,6 +164,18 @@ def muon_status_string(s: int) -> str:
 
 def muon_last_error(h=None) -> str:
     return load().muon_last_error(h).decode()
+
+
+def muon_lr_wsd(it: int, num_iterations: int, warmup_iters: int, warmdown_iters: int) -> float:
+    return load().muon_lr_wsd(it, num_iterations, warmup_iters, warmdown_iters)
+
+
+def muon_lr_cooldown_floor(step: int, main_iterations: int, cooldown_frac: float, floor: float) -> float:
+    return load().muon_lr_cooldown_floor(step, main_iterations, cooldown_frac, floor)
+
+
+def muon_momentum_warmup(step: int, warmup_steps: int, start: float, end: float) -> float:
+    return load().muon_momentum_warmup(step, warmup_steps, start, end)
 
 
 def _table(entries) -> "ctypes.Array":

@@ -19,8 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmuon.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "plan.cpp", "kernels_elementwise.hip", "kernels_ns.hip", "kernels_ns_mfma.hip",
-           "kernels_ns_small.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "schedule.cpp", "kernels_elementwise.hip", "kernels_ns.hip",
+           "kernels_ns_mfma.hip", "kernels_ns_small.hip"]
 ARCH = "gfx950"
 
 

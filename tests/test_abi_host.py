@@ -137,3 +137,48 @@ def test_null_handle_calls_are_safe():
     assert lib.muon_reset(None, None, 0, None) == B.MUON_E_INVALID_ARG
     assert lib.muon_num_matrices(None) == 0
     lib.muon_destroy(None)
+
+
+# ---- host-side schedules, pinned to the values the pages print ----
+
+def test_wsd_schedule_matches_the_pages():
+    # [P3] FlexAttention record: 1875 iterations, no warmup, warmdown 562 steps,
+    # "the warmdown starts at step 1313 and falls linearly to 0"
+    n, wd = 1875, 562
+    assert n - wd == 1313
+    assert B.muon_lr_wsd(0, n, 0, wd) == 1.0
+    assert B.muon_lr_wsd(1312, n, 0, wd) == 1.0
+    assert B.muon_lr_wsd(1313, n, 0, wd) == 1.0  # (n - it) / wd = 1 at the first warmdown step
+    assert math.isclose(B.muon_lr_wsd(1874, n, 0, wd), 1.0 / wd, rel_tol=1e-6)  # last step: one step from 0
+    assert all(B.muon_lr_wsd(i + 1, n, 0, wd) < B.muon_lr_wsd(i, n, 0, wd) for i in range(1313, 1874))
+    # [P4] 50B run: 95367 iterations, warmdown 27247 ("about 28.6% of training")
+    assert round(27247 / 95367 * 100, 1) == 28.6
+    assert B.muon_lr_wsd(95367 - 27247 - 1, 95367, 0, 27247) == 1.0
+    # halfway through the warmdown the multiplier is half (n - it = 13623 steps left of 27247)
+    assert math.isclose(B.muon_lr_wsd(95367 - 13623, 95367, 0, 27247), 13623 / 27247, rel_tol=1e-6)
+    # the Adam group's 500-step warmup: (it + 1) / 500
+    assert math.isclose(B.muon_lr_wsd(0, 95367, 500, 27247), 1 / 500, rel_tol=1e-6)
+    assert B.muon_lr_wsd(499, 95367, 500, 27247) == 1.0
+    assert math.isnan(B.muon_lr_wsd(n, n, 0, wd)) and math.isnan(B.muon_lr_wsd(-1, n, 0, wd))
+
+
+def test_cooldown_floor_schedule_matches_the_pages():
+    # [P2] change 3: last 80% of the main phase decays to the 0.30 floor, the
+    # 20 extension steps stay on the floor
+    main, frac, floor = 1000, 0.80, 0.30
+    assert B.muon_lr_cooldown_floor(0, main, frac, floor) == 1.0
+    assert B.muon_lr_cooldown_floor(200, main, frac, floor) == 1.0  # 1 - 0.8 of the way in: still flat
+    assert math.isclose(B.muon_lr_cooldown_floor(600, main, frac, floor), 0.30 + 0.70 * 0.5, rel_tol=1e-6)
+    for s in range(main, main + 20):
+        assert math.isclose(B.muon_lr_cooldown_floor(s, main, frac, floor), floor, rel_tol=1e-6)
+    vals = [B.muon_lr_cooldown_floor(s, main, frac, floor) for s in range(200, main + 1)]
+    assert all(a >= b for a, b in zip(vals, vals[1:]))
+
+
+def test_momentum_warmup_matches_the_pages():
+    # [P3]: frac = min(step / 500, 1), momentum from 0.85 to 0.95
+    assert math.isclose(B.muon_momentum_warmup(0, 500, 0.85, 0.95), 0.85, rel_tol=1e-6)
+    assert math.isclose(B.muon_momentum_warmup(250, 500, 0.85, 0.95), 0.90, rel_tol=1e-6)
+    assert math.isclose(B.muon_momentum_warmup(500, 500, 0.85, 0.95), 0.95, rel_tol=1e-6)
+    assert math.isclose(B.muon_momentum_warmup(10000, 500, 0.85, 0.95), 0.95, rel_tol=1e-6)
+    assert math.isnan(B.muon_momentum_warmup(-1, 500, 0.85, 0.95))
