@@ -235,6 +235,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="do not time kernels with events")
+    ap.add_argument("--stream-groups", type=int, default=3, help="stream groups of the timed pass (1 .. 4)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB once per pass (HBM counter calibration)")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
@@ -282,7 +283,7 @@ def main() -> int:
                 normuon=w.normuon, normuon_beta2=w.normuon_beta2, normuon_eps=w.normuon_eps,
                 weight_decay=w.weight_decay)
     # the step as shipped: tiled matrices split over two streams
-    H = B.MuonHandle(w.entries, B.make_hparams(**hpkw, stream_groups=2))
+    H = B.MuonHandle(w.entries, B.make_hparams(**hpkw, stream_groups=args.stream_groups))
     work = B.muon_work_stats(H.h)
     dev = torch.device("cuda:0")
     params = torch.from_numpy(gen_params(w)).to(dev)

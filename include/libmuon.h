@@ -80,15 +80,16 @@ enum { MUON_MOMENTUM_LERP = 0, MUON_MOMENTUM_HEAVY_BALL = 1 };
  *  ([P2] change 2); HEAVY_BALL: m <- beta m + g, Nesterov u = g + beta m
  *  ([P4] Muon source). ns_precision BF16: bf16 MFMA operands with fp32
  *  accumulation; FP32: fp32 throughout (debug / reference mode).
- *  stream_groups (not a method parameter; default 2): 2 lets muon_step split
- *  the tiled matrices into two cost-balanced groups when there are at least
- *  4 of them and their update output is at most 262144 tiles of 64 x 64
- *  (a few tile rounds of the GPU per launch). Each group runs its chain
- *  (momentum, Newton–Schulz, NorMuon, update) on its own stream: group 0 on
- *  the caller's stream, group 1 on a second, default-priority stream the
- *  handle owns, forked after group 0's momentum and joined at the end, so
- *  one group's kernels fill the other's tails and launch gaps. 1 keeps every
- *  launch on the caller's stream. Results are bit-identical either way. */
+ *  stream_groups (not a method parameter; 1 .. 4, default 3): G > 1 lets
+ *  muon_step split the tiled matrices into up to G cost-balanced groups, at
+ *  least 2 matrices per group, when their update output is at most 262144
+ *  tiles of 64 x 64 (a few tile rounds of the GPU per launch). Each group
+ *  runs its chain (momentum, Newton–Schulz, NorMuon, update) on its own
+ *  stream: group 0 on the caller's stream, group g > 0 on a default-priority
+ *  stream the handle owns, started after group g - 1's momentum and joined
+ *  back into the caller's stream at the end, so one group's kernels fill
+ *  the others' tails and launch gaps. 1 keeps every launch on the caller's
+ *  stream. Results are bit-identical for every value. */
 typedef struct muon_hparams {
     float momentum;
     int32_t nesterov;

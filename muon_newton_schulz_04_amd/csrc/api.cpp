@@ -33,14 +33,17 @@ struct muon_handle {
     bool profiling = false;
     std::vector<Rec> recs;          // recorded, not yet read
     std::vector<hipEvent_t> spare;  // events for reuse
-    // second stream group: its own stream (default priority, non-blocking)
-    // and the fork / join events that order it against the caller's stream
-    hipStream_t aux = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    // stream groups 1 .. n_groups - 1: their own streams (default priority,
+    // non-blocking), the events that start each one after the previous
+    // group's momentum, and the events that join them back
+    hipStream_t aux[muon::kMaxGroups - 1] = {};
+    hipEvent_t ev_fork[muon::kMaxGroups - 1] = {}, ev_join[muon::kMaxGroups - 1] = {};
     ~muon_handle() {
-        if (ev_fork) (void)hipEventDestroy(ev_fork);
-        if (ev_join) (void)hipEventDestroy(ev_join);
-        if (aux) (void)hipStreamDestroy(aux);
+        for (int g = 0; g < muon::kMaxGroups - 1; ++g) {
+            if (ev_fork[g]) (void)hipEventDestroy(ev_fork[g]);
+            if (ev_join[g]) (void)hipEventDestroy(ev_join[g]);
+            if (aux[g]) (void)hipStreamDestroy(aux[g]);
+        }
         for (auto& r : recs) {
             (void)hipEventDestroy(r.start);
             (void)hipEventDestroy(r.stop);
@@ -221,9 +224,11 @@ muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, co
         if (e == hipSuccess) e = up(L.off_poly, L.poly.data(), L.poly.size() * sizeof(muon::TileWork));
         if (e == hipSuccess) e = up(L.off_update, L.update.data(), L.update.size() * sizeof(muon::TileWork));
     }
-    if (e == hipSuccess && P.n_groups > 1) e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
-    if (e == hipSuccess && P.n_groups > 1) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
-    if (e == hipSuccess && P.n_groups > 1) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
+    for (int g = 0; g + 1 < P.n_groups && e == hipSuccess; ++g) {
+        e = hipStreamCreateWithFlags(&h->aux[g], hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork[g], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join[g], hipEventDisableTiming);
+    }
     if (e == hipSuccess && P.rows_total) e = hipMemset(h->ws + P.off_v, 0, (size_t)P.rows_total * 4);
     if (e == hipSuccess && P.mats.size()) e = hipMemset(h->ws + P.off_status, 0, P.mats.size() * 4);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -287,78 +292,88 @@ muon_status muon_step(muon_handle* h, float* params, const float* grads, float* 
     // Each stream group runs its whole chain: momentum of its matrices (and,
     // in group 0, the small-matrix Newton–Schulz), its tiled Newton–Schulz
     // launches, NorMuon and the parameter update. Group 0 runs on the
-    // caller's stream; group 1 runs on the handle's second stream, forked
-    // after group 0's momentum kernel and joined at the end. The stagger puts
-    // group 1's momentum under group 0's first GEMMs and group 0's update of
-    // the parameters under group 1's last GEMMs.
+    // caller's stream; group g > 0 on the handle's stream g - 1, which starts
+    // once group g - 1's momentum is done and joins the caller's stream at
+    // the end. The stagger puts each group's momentum under the previous
+    // groups' first GEMMs and the parameter updates under the last groups'
+    // GEMMs. Launches are issued iteration by iteration, round-robin over the
+    // groups, so every stream has work queued early.
+    std::vector<muon::LaunchCtx> Lg(P.n_groups, L);
+    std::vector<hipStream_t> sg(P.n_groups, st);
     for (int grp = 0; grp < P.n_groups; ++grp) {
-        const hipStream_t sg = grp == 0 ? st : h->aux;
-        muon::LaunchCtx Lg = L;
-        Lg.stream = sg;
-        Lg.ew_tile0 = P.ew_begin[grp];
-        Lg.ew_tiles = P.ew_begin[grp + 1] - P.ew_begin[grp];
-        Lg.active = L.active + P.act_begin[grp];
-        Lg.n_active = P.act_begin[grp + 1] - P.act_begin[grp];
-        s = run_on(sg, MUON_KERNEL_MOMENTUM, "momentum kernel", [&] {
-            return muon::launch_momentum(Lg, grads, momentum, beta, P.hp.nesterov,
+        sg[grp] = grp == 0 ? st : h->aux[grp - 1];
+        Lg[grp].stream = sg[grp];
+        Lg[grp].ew_tile0 = P.ew_begin[grp];
+        Lg[grp].ew_tiles = P.ew_begin[grp + 1] - P.ew_begin[grp];
+        Lg[grp].active = L.active + P.act_begin[grp];
+        Lg[grp].n_active = P.act_begin[grp + 1] - P.act_begin[grp];
+    }
+    for (int grp = 0; grp < P.n_groups; ++grp) {
+        s = run_on(sg[grp], MUON_KERNEL_MOMENTUM, "momentum kernel", [&] {
+            return muon::launch_momentum(Lg[grp], grads, momentum, beta, P.hp.nesterov,
                                          P.hp.momentum_kind == MUON_MOMENTUM_HEAVY_BALL);
         });
         if (s != MUON_OK) return s;
-        if (grp == 0 && P.n_groups > 1) {
-            e = hipEventRecord(h->ev_fork, st);
-            if (e == hipSuccess) e = hipStreamWaitEvent(h->aux, h->ev_fork, 0);
+        if (grp + 1 < P.n_groups) {
+            e = hipEventRecord(h->ev_fork[grp], sg[grp]);
+            if (e == hipSuccess) e = hipStreamWaitEvent(sg[grp + 1], h->ev_fork[grp], 0);
             if (e != hipSuccess) return hip_fail(h, e, "stream fork");
         }
-        if (grp == 0 && !P.small.empty()) {
-            muon::NsCoeffs co{};
-            std::memcpy(co.c, P.hp.ns_coeffs, sizeof(co.c));
-            co.steps = steps;
-            co.eps = P.hp.ns_eps;
-            s = run_on(sg, MUON_KERNEL_NS_SMALL, "small-matrix Newton-Schulz kernel", [&] {
-                return muon::launch_ns_small(Lg, reinterpret_cast<const int32_t*>(h->ws + P.off_small),
-                                             (int)P.small.size(), P.small_np, co, ns_out(h), P.hp.normuon);
-            });
-            if (s != MUON_OK) return s;
-        }
-        for (int k = 0; k < steps; ++k) {
-            void* xin = k == 0 ? L.xt : ((k & 1) ? L.x1 : L.x0);
-            void* xout = k == 0 ? L.x1 : ((k & 1) ? L.x0 : L.x1);
-            const float ca = P.hp.ns_coeffs[k][0], cb = P.hp.ns_coeffs[k][1], cc = P.hp.ns_coeffs[k][2];
-            const int first = k == 0;
-            const int rowstats = (k == steps - 1) && P.hp.normuon;
+    }
+    if (!P.small.empty()) {
+        muon::NsCoeffs co{};
+        std::memcpy(co.c, P.hp.ns_coeffs, sizeof(co.c));
+        co.steps = steps;
+        co.eps = P.hp.ns_eps;
+        s = run_on(sg[0], MUON_KERNEL_NS_SMALL, "small-matrix Newton-Schulz kernel", [&] {
+            return muon::launch_ns_small(Lg[0], reinterpret_cast<const int32_t*>(h->ws + P.off_small),
+                                         (int)P.small.size(), P.small_np, co, ns_out(h), P.hp.normuon);
+        });
+        if (s != MUON_OK) return s;
+    }
+    for (int k = 0; k < steps; ++k) {
+        void* xin = k == 0 ? L.xt : ((k & 1) ? L.x1 : L.x0);
+        void* xout = k == 0 ? L.x1 : ((k & 1) ? L.x0 : L.x1);
+        const float ca = P.hp.ns_coeffs[k][0], cb = P.hp.ns_coeffs[k][1], cc = P.hp.ns_coeffs[k][2];
+        const int first = k == 0;
+        const int rowstats = (k == steps - 1) && P.hp.normuon;
+        for (int grp = 0; grp < P.n_groups; ++grp) {
             for (const auto& T : P.lists) {
                 if (T.group != grp) continue;
                 const muon::GemmList G = make_list(h, T);
                 const bool big = !L.fp32 && G.T >= 128;
+                const muon::LaunchCtx& C = Lg[grp];
                 auto stage = [&](int mode, const void* x, const void* a, void* o, int rs) {
-                    return big ? muon::launch_ns_stage_big(Lg, G, mode, x, a, o, ca, cb, cc, first, P.hp.ns_eps, rs)
-                               : muon::launch_ns_stage(Lg, G, mode, x, a, o, ca, cb, cc, first, P.hp.ns_eps, rs);
+                    return big ? muon::launch_ns_stage_big(C, G, mode, x, a, o, ca, cb, cc, first, P.hp.ns_eps, rs)
+                               : muon::launch_ns_stage(C, G, mode, x, a, o, ca, cb, cc, first, P.hp.ns_eps, rs);
                 };
-                s = run_on(sg, MUON_KERNEL_GRAM, "Gram kernel",
+                s = run_on(sg[grp], MUON_KERNEL_GRAM, "Gram kernel",
                            [&] { return stage(muon::NS_GRAM, xin, nullptr, L.a, 0); });
                 if (s != MUON_OK) return s;
-                s = run_on(sg, MUON_KERNEL_POLY, "polynomial kernel",
+                s = run_on(sg[grp], MUON_KERNEL_POLY, "polynomial kernel",
                            [&] { return stage(muon::NS_POLY, nullptr, L.a, L.b, 0); });
                 if (s != MUON_OK) return s;
-                s = run_on(sg, MUON_KERNEL_UPDATE, "update kernel",
+                s = run_on(sg[grp], MUON_KERNEL_UPDATE, "update kernel",
                            [&] { return stage(muon::NS_UPDATE, xin, L.b, xout, rowstats); });
                 if (s != MUON_OK) return s;
             }
         }
+    }
+    for (int grp = 0; grp < P.n_groups; ++grp) {
         const float* f = nullptr;
         if (P.hp.normuon) {
-            s = run_on(sg, MUON_KERNEL_NORMUON, "NorMuon kernel",
-                       [&] { return muon::launch_normuon(Lg, P.hp.normuon_beta2, P.hp.normuon_eps); });
+            s = run_on(sg[grp], MUON_KERNEL_NORMUON, "NorMuon kernel",
+                       [&] { return muon::launch_normuon(Lg[grp], P.hp.normuon_beta2, P.hp.normuon_eps); });
             if (s != MUON_OK) return s;
             f = L.f;
         }
-        s = run_on(sg, MUON_KERNEL_APPLY, "apply kernel",
-                   [&] { return muon::launch_apply(Lg, ns_out(h), f, params, lr, P.hp.weight_decay); });
+        s = run_on(sg[grp], MUON_KERNEL_APPLY, "apply kernel",
+                   [&] { return muon::launch_apply(Lg[grp], ns_out(h), f, params, lr, P.hp.weight_decay); });
         if (s != MUON_OK) return s;
     }
-    if (P.n_groups > 1) {
-        e = hipEventRecord(h->ev_join, h->aux);
-        if (e == hipSuccess) e = hipStreamWaitEvent(st, h->ev_join, 0);
+    for (int grp = 1; grp < P.n_groups; ++grp) {
+        e = hipEventRecord(h->ev_join[grp - 1], sg[grp]);
+        if (e == hipSuccess) e = hipStreamWaitEvent(st, h->ev_join[grp - 1], 0);
         if (e != hipSuccess) return hip_fail(h, e, "stream join");
     }
     return MUON_OK;

@@ -120,11 +120,14 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     using LY = Layout<T, BK>;
     constexpr int KROWB = LY::KROWB;
     constexpr int EROW = 2 * T + 8;                  // epilogue staging row (bytes)
-    constexpr int SMEM = NBUF * LY::STAGE > T * EROW ? NBUF * LY::STAGE : T * EROW;
-    static_assert(FRJ >= 1 && NWV % 2 == 0, "tile too small for this wave grid");
+    // the ring, or the epilogue's staged rows plus a small reduction area at
+    // the top (the Gram's first-iteration norm; the ring is idle by then)
+    constexpr int REDB = 64;
+    constexpr int SMEM = NBUF * LY::STAGE > T * EROW + REDB ? NBUF * LY::STAGE : T * EROW + REDB;
+    static_assert(FRJ >= 1 && NWV % 2 == 0 && NWV * 4 <= REDB, "tile too small for this wave grid");
 
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
-    __shared__ float red[NWV];
+    float* red = reinterpret_cast<float*>(smem + SMEM - REDB);
 
     const TileWork w = work[blockIdx.x];
     const MatDesc d = mats[w.mat];
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     };
 
     const int nk = K / BK;  // >= 2 (K >= 128)
-    static_assert(D <= 3, "ring depth");
+    static_assert(D <= 4, "ring depth");
     auto buf = [&](int k) { return smem + (k % NBUF) * LY::STAGE; };
 #pragma unroll
     for (int k = 0; k < D; ++k) dma_stage(k, buf(k));
@@ -355,9 +358,11 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     read_frags(buf(0), 0, 0);
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
     using CD = std::integral_constant<int, D - 1>;
     using CL = std::integral_constant<int, -1>;
     for (int kt = 0; kt < nk - D; ++kt) stage(buf(kt), buf(kt + 1), buf(kt + D), kt, std::true_type{}, CD{});
+    if constexpr (D >= 4) stage(buf(nk - 4), buf(nk - 3), buf(nk), nk - 4, std::false_type{}, C2{});
     if constexpr (D >= 3) stage(buf(nk - 3), buf(nk - 2), buf(nk), nk - 3, std::false_type{}, C1{});
     if constexpr (D >= 2) stage(buf(nk - 2), buf(nk - 1), buf(nk + 1), nk - 2, std::false_type{}, C0{});
     stage(buf(nk - 1), buf(nk), buf(nk + 2), nk - 1, std::false_type{}, CL{});

@@ -55,7 +55,7 @@ muon_status check_hparams(const muon_hparams* hp, std::string* err) {
         return bad("normuon_beta2 must be in [0, 1]");
     if (!finite(hp->normuon_eps) || hp->normuon_eps < 0.f) return bad("normuon_eps must be finite and >= 0");
     if (!finite(hp->weight_decay)) return bad("weight_decay must be finite");
-    if (hp->stream_groups != 1 && hp->stream_groups != 2) return bad("stream_groups must be 1 or 2");
+    if (hp->stream_groups < 1 || hp->stream_groups > kMaxGroups) return bad("stream_groups must be in [1, 4]");
     return MUON_OK;
 }
 
@@ -234,15 +234,16 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
             cost.push_back({m * (m + 1) * nn + m * (m + 1) * m + 2 * m * m * nn, mi});
             tiles64 += (int64_t)(d.m_pad / 64) * (d.n_pad / 64);
         }
-        if (P.hp.stream_groups > 1 && cost.size() >= (size_t)kMinSplit && tiles64 <= kMaxSplitTiles64) {
-            P.n_groups = 2;
+        const int ng = std::min<int>(P.hp.stream_groups, (int)(cost.size() / kMinSplit));
+        if (ng > 1 && tiles64 <= kMaxSplitTiles64) {
+            P.n_groups = ng;
             std::stable_sort(cost.begin(), cost.end(),
                              [](const std::pair<double, int32_t>& a, const std::pair<double, int32_t>& b) {
                                  return a.first > b.first;
                              });
-            double load[2] = {0.0, 0.0};
+            double load[kMaxGroups] = {};
             for (const auto& c : cost) {
-                const int g = load[0] <= load[1] ? 0 : 1;
+                const int g = (int)(std::min_element(load, load + ng) - load);
                 group_of[c.second] = g;
                 load[g] += c.first;
             }
@@ -362,5 +363,5 @@ extern "C" void muon_hparams_default(muon_hparams* hp) {
     hp->normuon_beta2 = 0.95f;
     hp->normuon_eps = 1e-10f;
     hp->weight_decay = 0.0f;
-    hp->stream_groups = 2;
+    hp->stream_groups = 3;
 }

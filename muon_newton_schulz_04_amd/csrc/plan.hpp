@@ -14,12 +14,13 @@
 
 namespace muon {
 
-// Tiled matrices needed before the Newton–Schulz launches are split over two
-// streams (fewer gain nothing from the overlap), and the most update tiles
+// At most kMaxGroups stream groups; a split needs kMinSplit tiled matrices
+// per group (fewer gain nothing from the overlap), and the most update tiles
 // (in 64 x 64 units) a step may have for the split: beyond that each launch
 // runs so many tile rounds that its tail is negligible, and two groups in
 // flight only double the working set in L2 / MALL.
-constexpr int kMinSplit = 4;
+constexpr int kMaxGroups = 4;
+constexpr int kMinSplit = 2;
 constexpr int64_t kMaxSplitTiles64 = (int64_t)64 * 256 * 16;
 
 struct TileList {
@@ -44,8 +45,8 @@ struct Plan {
     // the active matrices are ordered group by group (small matrices in
     // group 0), and so are their elementwise tiles: group g owns active[
     // act_begin[g] .. act_begin[g+1]) and tiles [ew_begin[g], ew_begin[g+1])
-    int act_begin[3] = {0, 0, 0};
-    int ew_begin[3] = {0, 0, 0};
+    int act_begin[kMaxGroups + 1] = {};
+    int ew_begin[kMaxGroups + 1] = {};
     std::vector<int32_t> small;         // active matrices of the one-workgroup Newton–Schulz
     int small_np = 0;                   // their largest n_pad
     size_t off_small = 0;

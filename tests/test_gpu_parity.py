@@ -99,20 +99,21 @@ LARGE_TILES = [
 
 
 def test_stream_groups_give_identical_results():
-    # the tiled matrices split over two streams (default) or all on the
+    # the 9 tiled matrices split over 2, 3 or 4 streams, or all on the
     # caller's stream: the same kernels on the same tiles, so bit-identical
     w = custom_workload(110, LARGE_TILES + [(200, 300, 2, "spike"), (64, 64, 3, "rank8")], steps=2, lr=0.05,
                         weight_decay=0.1, normuon=1)
-    runs = [GpuRun(w, stream_groups=g) for g in (1, 2)]
+    runs = [GpuRun(w, stream_groups=g) for g in (1, 2, 3, 4)]
     for t in range(2):
         for r in runs:
             r.load_grads(t)
             r.step()
-        for name in ("params", "mom"):
-            a, b = getattr(runs[0], name), getattr(runs[1], name)
-            assert torch.equal(a, b), f"step {t}: {name} differs between one and two stream groups"
-        assert torch.equal(runs[0].H.view(B.MUON_VIEW_NS_OUT, torch.bfloat16),
-                           runs[1].H.view(B.MUON_VIEW_NS_OUT, torch.bfloat16))
+        for g, r in enumerate(runs[1:], start=2):
+            for name in ("params", "mom"):
+                assert torch.equal(getattr(runs[0], name), getattr(r, name)), \
+                    f"step {t}: {name} differs between one and {g} stream groups"
+            assert torch.equal(runs[0].H.view(B.MUON_VIEW_NS_OUT, torch.bfloat16),
+                               r.H.view(B.MUON_VIEW_NS_OUT, torch.bfloat16))
 
 
 def test_step_captured_in_a_hip_graph_replays_like_eager():
