@@ -157,7 +157,7 @@ def _short_kernel(name: str) -> str:
 
 def trace_summary(trace_dir: str, workload: str, command: str) -> str:
     """Markdown table of a rocprofv3 --kernel-trace run: per kernel and grid
-    size (the two-stream launches of a stage have smaller grids than the
+    size (the stream-group launches of a stage have smaller grids than the
     one-stream launches of the kernel pass), calls and durations."""
     import csv
     import glob
@@ -177,7 +177,8 @@ def trace_summary(trace_dir: str, workload: str, command: str) -> str:
     out = [f"# rocprofv3 kernel trace — Muon step, {workload}", "",
            "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
            f"Kernel sources hash (bench.py `source_hash`): `{_kernel_source_hash()}`. The bench runs the timed steps "
-           "with the shipped two-stream schedule (a stage's launches split over two streams, smaller grids), then "
+           "with the shipped stream-group schedule (a stage's launches split over up to three streams, smaller "
+           "grids), then "
            "the kernel pass with every launch on one stream (full grids); the roofline uses the full-grid rows.", "",
            "| kernel | workgroups | calls | avg µs | median µs | min µs | max µs | share |",
            "|---|---|---|---|---|---|---|---|"]
@@ -282,7 +283,7 @@ def main() -> int:
     hpkw = dict(momentum=w.momentum, nesterov=w.nesterov, ns_steps=w.ns_steps, precision=w.ns_precision,
                 normuon=w.normuon, normuon_beta2=w.normuon_beta2, normuon_eps=w.normuon_eps,
                 weight_decay=w.weight_decay)
-    # the step as shipped: tiled matrices split over two streams
+    # the step as shipped: tiled matrices split over stream groups
     H = B.MuonHandle(w.entries, B.make_hparams(**hpkw, stream_groups=args.stream_groups))
     work = B.muon_work_stats(H.h)
     dev = torch.device("cuda:0")
@@ -299,7 +300,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # timed region: whole steps, no per-launch events (they would serialise
-    # the two stream groups)
+    # the stream groups)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
@@ -392,7 +393,7 @@ def main() -> int:
         "roofline": roofline,
         "kernels": kernels,
         "kernels_pass": "a second pass of the same steps with every launch on one stream (stream_groups=1), "
-                        "each timed with HIP events; the timed region above runs the shipped two-stream "
+                        "each timed with HIP events; the timed region above runs the shipped stream-group "
                         "schedule without per-launch events",
         "wall_s": wall,
         "device": torch.cuda.get_device_name(0),
