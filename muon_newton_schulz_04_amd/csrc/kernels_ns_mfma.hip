@@ -47,6 +47,7 @@ namespace muon {
 namespace {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 // K pipeline per stage kind: BK-wide K slices through NBUF LDS buffers, the
@@ -464,7 +465,10 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
                 lds64((wi * WTM + fi * 32 + l32) * EROW + 2 * (wj * WTN + fj * 32 + 8 * g + 4 * hi)) = ev[fi][fj][g];
     __syncthreads();
 
-    // the tile itself: each thread moves 16-byte row chunks, a wave covers whole rows
+    // the tile itself: each thread moves 16-byte row chunks, a wave covers
+    // whole rows. The update's output is stored nontemporally: a round of
+    // tiles writes about as much as an XCD's L2 holds, and normal stores
+    // would push out the B and X panels the next round reads.
     {
         bf16* obase = MODE == NS_UPDATE ? out + d.x_off + (int64_t)i0 * d.n_pad + j0
                                         : out + d.a_off + (int64_t)i0 * d.m_pad + j0;
@@ -476,27 +480,35 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             const int r = id / CPR, c = id % CPR;
             const uint2 lo = lds64(r * EROW + 16 * c);
             const uint2 up = lds64(r * EROW + 16 * c + 8);
-            *reinterpret_cast<uint4*>(obase + (int64_t)r * ld + 8 * c) = make_uint4(lo.x, lo.y, up.x, up.y);
+            const u32x4 wv = {lo.x, lo.y, up.x, up.y};
+            if (MODE == NS_UPDATE)
+                __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(obase + (int64_t)r * ld + 8 * c));
+            else
+                *reinterpret_cast<u32x4*>(obase + (int64_t)r * ld + 8 * c) = wv;
         }
     }
     if (MODE != NS_UPDATE && w.ti != w.tj) {
-        // the mirror tile, read column-wise with ds_read_b64_tr_b16: in each
-        // 16-lane group G, lane s = 4e + q points at row IB + 16G + 4q + e of
-        // column chunk JB, so lane 4q + c receives rows IB + 16G + 4q .. +3 of
-        // column JB + c; the 16 lanes with the same c then hold 64 consecutive
-        // entries (one 128-byte line) of mirror row JB + c.
+        // the mirror tile, read column-wise with two ds_read_b64_tr_b16 per
+        // lane: in each 16-lane group G, lane s = 4 e + q points at row
+        // IB + 32 G + 8 q + e (then + 4) of the 4-column chunk JB, so lane
+        // 4 q + c receives rows IB + 32 G + 8 q .. +7 of column JB + c and
+        // stores them as 16 bytes of mirror row JB + c; the 16 lanes with the
+        // same c cover 128 consecutive entries (two cache lines) of that row.
         bf16* mbase = out + d.a_off + (int64_t)j0 * d.m_pad + i0;
         const int G = lane >> 4, sl = lane & 15;
-        const int sup_row = 16 * G + 4 * (sl & 3) + (sl >> 2);
+        const int sup_row = 32 * G + 8 * (sl & 3) + (sl >> 2);
         const int rc = sl & 3, rq = sl >> 2;
-        constexpr int NIT = (T / 4) * (T / 64) / NWV;  // instructions per wave
+        constexpr int NIT = (T / 4) * (T / 128) / NWV;  // instruction pairs per wave
+        static_assert(NIT * NWV == (T / 4) * (T / 128), "mirror work split");
 #pragma unroll 4
         for (int k = 0; k < NIT; ++k) {
             const int it = wave + NWV * k;
             const int JB = 4 * (it % (T / 4));
-            const int IB = 64 * (it / (T / 4));
-            const bf16x4 v = tr_read(smem + (IB + sup_row) * EROW + 2 * JB);
-            *reinterpret_cast<bf16x4*>(mbase + (int64_t)(JB + rc) * d.m_pad + IB + 16 * G + 4 * rq) = v;
+            const int IB = 128 * (it / (T / 4));
+            const bf16x4 lo = tr_read(smem + (IB + sup_row) * EROW + 2 * JB);
+            const bf16x4 up = tr_read(smem + (IB + sup_row + 4) * EROW + 2 * JB);
+            const bf16x8 v = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+            *reinterpret_cast<bf16x8*>(mbase + (int64_t)(JB + rc) * d.m_pad + IB + 32 * G + 8 * rq) = v;
         }
     }
 
