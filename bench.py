@@ -96,18 +96,8 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str) -> dict:
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            if "neg_kernel" in name:
-                key = "copy"
-            elif "k_ns_big<" in name or "k_ns<" in name:
-                mode = name.split("<", 1)[1].split(">", 1)[0].split(",")
-                key = {"0": "gram", "1": "poly", "2": "update"}[mode[-2].strip() if "big" in name else mode[2].strip()]
-            elif "k_ns_small" in name:
-                key = "ns_small"
-            elif "k_momentum" in name:
-                key = "momentum"
-            elif "k_apply" in name:
-                key = "apply"
-            else:
+            key = _kernel_class(name)
+            if not key:
                 unmatched.add(name[:80])
                 continue
             grid = int(r["Grid_Size"])
@@ -136,6 +126,72 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str) -> dict:
     if unmatched:
         print("unmatched kernels:", sorted(unmatched), file=sys.stderr)
     return out
+
+
+def _ns_alg_flops(workload) -> dict:
+    """Algorithmic FLOP of one GRAM / POLY / UPDATE launch over every active
+    bf16 matrix of a workload (symmetric Gram and A A count m(m+1) k)."""
+    out = {"gram": 0.0, "poly": 0.0, "update": 0.0}
+    for e in workload.entries:
+        if e.frozen:
+            continue
+        m, n = min(e.rows, e.cols), max(e.rows, e.cols)
+        out["gram"] += e.count * m * (m + 1) * n
+        out["poly"] += e.count * m * (m + 1) * m
+        out["update"] += e.count * 2 * m * m * n
+    return out
+
+
+def mfma_summary(pmc_dir: str, workload_id: int) -> dict:
+    """MFMA utilisation of each NS kernel class from one rocprofv3 --pmc run
+    (MfmaUtil, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16): rocprofiler's derived MfmaUtil (MFMA busy
+    cycles summed over all SIMDs / (the largest per-XCD GUI-active count x
+    SIMDs)) and the bf16 MFMA work executed against the algorithmic work,
+    medians over the largest-grid dispatches (the one-stream kernel pass)."""
+    import statistics
+    from workloads import get_workload
+    w = get_workload(workload_id)
+    alg = _ns_alg_flops(w)
+    per = {}
+    for r in _pmc_rows(pmc_dir):
+        key = _kernel_class(r["Kernel_Name"])
+        if key not in ("gram", "poly", "update"):
+            continue
+        d = per.setdefault(key, {}).setdefault(int(r["Grid_Size"]), {})
+        d.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    out = {"workload": w.name, "source_hash": _kernel_source_hash(),
+           "commands": ["cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc MfmaUtil "
+                        "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d "
+                        "$REPO/gpurun_out/pmc_mfma2 -o run -- python3 $REPO/bench.py --steps 3 --warmup 1 "
+                        "--no-cpu-baseline",
+                        "python3 bench.py --pmc-mfma-summary gpurun_out/pmc_mfma2"],
+           "note": "mfma_util_pct is rocprofiler's MfmaUtil (sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (max over "
+                   "the XCDs of GRBM_GUI_ACTIVE x SIMDs) x 100); executed_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; "
+                   "alg_flop counts the symmetric Gram and A A as m(m+1)k, so executed / alg > 1 is the diagonal "
+                   "tiles' lower halves and the padding",
+           "kernels": {}}
+    for key, grids in per.items():
+        launches = list(grids[max(grids)].values())
+        util = statistics.median(d["MfmaUtil"] for d in launches)
+        ex = statistics.median(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0 for d in launches)
+        out["kernels"][key] = {"dispatches": len(launches), "mfma_util_pct": util, "executed_flop": ex,
+                               "alg_flop": alg[key], "executed_over_alg": ex / alg[key] if alg[key] else None,
+                               "mfma_busy_cycles": statistics.median(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in launches)}
+    return out
+
+
+def _kernel_class(name: str) -> str:
+    """gram / poly / update / ns_small / momentum / apply / copy for a kernel name, or '' otherwise."""
+    if "neg_kernel" in name:
+        return "copy"
+    if "k_ns_big<" in name or "k_ns<" in name:
+        mode = name.split("<", 1)[1].split(">", 1)[0].split(",")
+        return {"0": "gram", "1": "poly", "2": "update"}[mode[-2].strip() if "big" in name else mode[2].strip()]
+    for k in ("ns_small", "momentum", "apply"):
+        if "k_" + k in name:
+            return k
+    return ""
 
 
 def _short_kernel(name: str) -> str:
@@ -241,6 +297,9 @@ def main() -> int:
                     help="after the timed steps, copy 1 GiB once per pass (HBM counter calibration)")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
                     help="summarise a rocprofv3 --kernel-trace run into profiles/kernel_stats_<workload>.md and exit")
+    ap.add_argument("--pmc-mfma-summary", metavar="PMC_DIR",
+                    help="summarise a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16 into profiles/mfma_<workload>.json and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into "
                          "profiles/traffic_<workload>.json and exit")
@@ -253,6 +312,14 @@ def main() -> int:
         with open(os.path.join(ROOT, "profiles", f"kernel_stats_{wname}.md"), "w") as f:
             f.write(md)
         print(md)
+        return 0
+
+    if args.pmc_mfma_summary:
+        t = mfma_summary(args.pmc_mfma_summary, args.config)
+        path = os.path.join(ROOT, "profiles", f"mfma_{t['workload']}.json")
+        with open(path, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t, indent=1))
         return 0
 
     if args.pmc_summary:
