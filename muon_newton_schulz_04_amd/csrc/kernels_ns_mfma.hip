@@ -74,10 +74,6 @@ __device__ __forceinline__ bf16x4 tr_read(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(LDS_AS char*)p);
 }
 
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
 // 16 bytes per lane, global -> LDS: lane i lands at lds + 16 i (lds is
 // wave-uniform, passed in M0). Issued as inline assembly so that the compiler
 // does not track these LDS writes: it would otherwise wait for every load in
@@ -95,6 +91,38 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int v
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// The 32 x 32 blocks a wave computes on a diagonal tile (on or above the
+// diagonal), as a bit mask over f = fi * 2 + fj: the wave (wi, wj) of a
+// 2 x WN grid owns row blocks wi FRI + fi and column blocks wj, 2 WN - 1 - wj.
+constexpr unsigned diag_mask(int wi, int wj, int WN, int FRI) {
+    unsigned m = 0;
+    for (int fi = 0; fi < FRI; ++fi)
+        for (int fj = 0; fj < 2; ++fj) {
+            const int c = fj == 0 ? wj : 2 * WN - 1 - wj;
+            if (c >= wi * FRI + fi) m |= 1u << (fi * 2 + fj);
+        }
+    return m;
+}
+constexpr int bit_count(unsigned m) { return m ? (int)(m & 1u) + bit_count(m >> 1) : 0; }
+// the position of the k-th set bit of m
+constexpr int nth_bit(unsigned m, int k) {
+    for (int b = 0; b < 32; ++b)
+        if ((m >> b) & 1u) {
+            if (k == 0) return b;
+            --k;
+        }
+    return -1;
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // s_waitcnt vmcnt(0), leaving the LDS / scalar counters alone
@@ -143,6 +171,13 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     const int hi = lane >> 5;
     // diagonal Gram / polynomial tile: both operands are the same rows
     const bool same = MODE != NS_UPDATE && w.ti == w.tj;
+    // The wave's 32-row fragment blocks are wi FRI + fi; its two 32-column
+    // blocks are wj and 2 WN - 1 - wj, so that on a diagonal tile the two
+    // waves of every SIMD hold the same number of blocks on or above the
+    // diagonal (9 of 16 at T = 256) and skipping the others shortens the tile.
+    static_assert(FRJ == 2, "two fragment columns per wave");
+    const int cb1 = 2 * WN - 1 - wj;
+    auto colblk = [&](int fj) { return fj == 0 ? wj : cb1; };
 
     const bf16* Psrc;
     const bf16* Qsrc;
@@ -238,7 +273,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) fo[ks] = l32 * KROWB + 16 * ((2 * ks + hi) ^ ((l32 >> SH) & (CPRK - 1)));
     const int pb = wi * WTM * KROWB;
-    const int qb = wj * WTN * KROWB + (same ? 0 : LY::KTILE);
+    const int qb = same ? 0 : LY::KTILE;
     // X (update): lane s of 16-lane group g reads row 8 (g >> 1) + (s >> 2) (+ 16 ks + 4 h),
     // elements wj WTN + 32 f + 16 (g & 1) + 4 (s & 3) .. +3
     const int g16 = lane >> 4;
@@ -247,7 +282,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     int tb[FRJ];
 #pragma unroll
     for (int f = 0; f < FRJ; ++f) {
-        const int e = wj * WTN + 32 * f + 16 * (g16 & 1) + 4 * (s16 & 3);
+        const int e = 32 * colblk(f) + 16 * (g16 & 1) + 4 * (s16 & 3);
         tb[f] = LY::KTILE + trow * LY::XROWB + 16 * ((e >> 3) ^ (4 * (trow & 3))) + 2 * (e & 7);
     }
 
@@ -260,7 +295,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
 #pragma unroll
         for (int f = 0; f < FRJ; ++f) {
             if (MODE != NS_UPDATE) {
-                qfr[set][f] = *reinterpret_cast<const bf16x8*>(S + qb + fo[ks] + f * 32 * KROWB);
+                qfr[set][f] = *reinterpret_cast<const bf16x8*>(S + qb + fo[ks] + colblk(f) * 32 * KROWB);
             } else {
                 const bf16x4 lo = tr_read(S + tb[f] + (16 * ks) * LY::XROWB);
                 const bf16x4 up = tr_read(S + tb[f] + (16 * ks + 4) * LY::XROWB);
@@ -290,12 +325,18 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
 
     constexpr int NREAD = FRI + (MODE == NS_UPDATE ? 2 : 1) * FRJ;  // LDS read instructions per sub-step
 
-    auto mfma_block = [&](int set, int lo, int hi_) {
-#pragma unroll
-        for (int f = lo; f < hi_; ++f) {
-            const int fi = f / FRJ, fj = f % FRJ;
+    // MASK: the blocks this wave computes (all of them, or on a diagonal
+    // Gram / polynomial tile those on or above the diagonal; the epilogue
+    // writes the others from their mirror images). lo .. hi_ index the set
+    // bits of MASK, so the instruction stream is fixed at compile time.
+    auto mfma_block = [&](int set, auto lo_c, auto hi_c, auto mask_c) {
+        constexpr unsigned MASK = decltype(mask_c)::value;
+        constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+        static_for<LO, HI>([&](auto k_c) {
+            constexpr int f = nth_bit(MASK, decltype(k_c)::value);
+            constexpr int fi = f / FRJ, fj = f % FRJ;
             acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[set][fj], pfr[set][fi], acc[fi][fj], 0, 0, 0);
-        }
+        });
     };
     // One K stage (kt) of the NBUF-deep ring. S: its buffer; N1: the next
     // stage's; NL: the buffer the previous stage released, which receives
@@ -306,16 +347,19 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     // of S; the explicit waits and barriers order the ring.
     constexpr int NKS = BK / 16;  // k16 sub-steps per stage
     auto stage = [&](const char* __restrict__ S, const char* __restrict__ N1, char* __restrict__ NL, int kt,
-                     auto load_c, auto wait_c) {
+                     auto load_c, auto wait_c, auto mask_c) {
         constexpr bool LOAD = decltype(load_c)::value;
         constexpr int WAIT = decltype(wait_c)::value;
-        constexpr int NF = FRI * FRJ;
+        constexpr int NF = bit_count(decltype(mask_c)::value);
+        using IC0 = std::integral_constant<int, 0>;
+        using ICH = std::integral_constant<int, NF / 2>;
+        using ICN = std::integral_constant<int, NF>;
         if constexpr (LOAD) dma_stage(kt + D, NL);
 #pragma unroll
         for (int ks = 0; ks < NKS - 1; ++ks) {
             const int set = ks & 1;
             read_frags(S, ks + 1, set ^ 1);
-            mfma_block(set, 0, NF);
+            mfma_block(set, IC0{}, ICN{}, mask_c);
             // interleave: one MFMA, then one LDS read
 #pragma unroll
             for (int i = 0; i < NF; ++i) {
@@ -327,12 +371,12 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         // next stage's first fragment reads run under the second half
         constexpr int SL = (NKS - 1) & 1;
         if constexpr (WAIT >= 0) {
-            mfma_block(SL, 0, NF / 2);
+            mfma_block(SL, IC0{}, ICH{}, mask_c);
             __builtin_amdgcn_sched_barrier(0);  // keep these MFMAs ahead of the wait
             wait_stage(std::integral_constant<int, WAIT>{});
             __syncthreads();
             read_frags(N1, 0, 0);
-            mfma_block(SL, NF / 2, NF);
+            mfma_block(SL, ICH{}, ICN{}, mask_c);
 #pragma unroll
             for (int i = 0; i < NF / 2; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -344,7 +388,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
 #pragma unroll
                 for (int q = 0; q < NAP && q < NBUF - 1; ++q) dma_apart(q, smem + ((kt + 1 + q) % NBUF) * LY::STAGE);
             }
-            mfma_block(SL, 0, NF);
+            mfma_block(SL, IC0{}, ICN{}, mask_c);
             __syncthreads();
         }
     };
@@ -362,11 +406,23 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     using C2 = std::integral_constant<int, 2>;
     using CD = std::integral_constant<int, D - 1>;
     using CL = std::integral_constant<int, -1>;
-    for (int kt = 0; kt < nk - D; ++kt) stage(buf(kt), buf(kt + 1), buf(kt + D), kt, std::true_type{}, CD{});
-    if constexpr (D >= 4) stage(buf(nk - 4), buf(nk - 3), buf(nk), nk - 4, std::false_type{}, C2{});
-    if constexpr (D >= 3) stage(buf(nk - 3), buf(nk - 2), buf(nk), nk - 3, std::false_type{}, C1{});
-    if constexpr (D >= 2) stage(buf(nk - 2), buf(nk - 1), buf(nk + 1), nk - 2, std::false_type{}, C0{});
-    stage(buf(nk - 1), buf(nk), buf(nk + 2), nk - 1, std::false_type{}, CL{});
+    auto main_loop = [&](auto mask_c) {
+        for (int kt = 0; kt < nk - D; ++kt) stage(buf(kt), buf(kt + 1), buf(kt + D), kt, std::true_type{}, CD{}, mask_c);
+        if constexpr (D >= 4) stage(buf(nk - 4), buf(nk - 3), buf(nk), nk - 4, std::false_type{}, C2{}, mask_c);
+        if constexpr (D >= 3) stage(buf(nk - 3), buf(nk - 2), buf(nk), nk - 3, std::false_type{}, C1{}, mask_c);
+        if constexpr (D >= 2) stage(buf(nk - 2), buf(nk - 1), buf(nk + 1), nk - 2, std::false_type{}, C0{}, mask_c);
+        stage(buf(nk - 1), buf(nk), buf(nk + 2), nk - 1, std::false_type{}, CL{}, mask_c);
+    };
+    constexpr unsigned FULL = (1u << (FRI * FRJ)) - 1;
+    if (MODE == NS_UPDATE || !same) {
+        main_loop(std::integral_constant<unsigned, FULL>{});
+    } else {
+        // a diagonal tile: each wave type runs its own fixed block list
+        static_for<0, NWV>([&](auto w_c) {
+            constexpr int W = decltype(w_c)::value;
+            if (wave == W) main_loop(std::integral_constant<unsigned, diag_mask(W / WN, W % WN, WN, FRI)>{});
+        });
+    }
     if constexpr (MODE == NS_POLY) {
         if constexpr (NAP == NBUF) dma_apart(NBUF - 1, buf(nk + NBUF - 1));
         wait_vm0();
@@ -419,13 +475,13 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         for (int fj = 0; fj < FRJ; ++fj) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int jl = wj * WTN + fj * 32 + 8 * g + 4 * hi;
+                const int jl = 32 * colblk(fj) + 8 * g + 4 * hi;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[fi][fj][4 * g + e];
                 if (MODE == NS_POLY) {
                     // P = a I + b A + c A A: the a X term of the update rides on P's diagonal
-                    const int c = ((wj * WTN + fj * 32) >> 3) + g;
+                    const int c = 4 * colblk(fj) + g;
                     const uint2 in =
                         *reinterpret_cast<const uint2*>(abase(il) + 16 * (c ^ asw));
                     v[0] = fmaf(cb, bf16_lo(in.x), cc * v[0]);
@@ -462,7 +518,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         for (int fj = 0; fj < FRJ; ++fj)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                lds64((wi * WTM + fi * 32 + l32) * EROW + 2 * (wj * WTN + fj * 32 + 8 * g + 4 * hi)) = ev[fi][fj][g];
+                lds64((wi * WTM + fi * 32 + l32) * EROW + 2 * (32 * colblk(fj) + 8 * g + 4 * hi)) = ev[fi][fj][g];
     __syncthreads();
 
     // the tile itself: each thread moves 16-byte row chunks, a wave covers
@@ -478,6 +534,8 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         for (int q = 0; q < T * CPR / NT; ++q) {
             const int id = tid + NT * q;
             const int r = id / CPR, c = id % CPR;
+            // a diagonal tile's blocks below the diagonal come from the mirror below
+            if (MODE != NS_UPDATE && same && (c >> 2) < (r >> 5)) continue;
             const uint2 lo = lds64(r * EROW + 16 * c);
             const uint2 up = lds64(r * EROW + 16 * c + 8);
             const u32x4 wv = {lo.x, lo.y, up.x, up.y};
@@ -487,13 +545,15 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
                 *reinterpret_cast<u32x4*>(obase + (int64_t)r * ld + 8 * c) = wv;
         }
     }
-    if (MODE != NS_UPDATE && w.ti != w.tj) {
+    if (MODE != NS_UPDATE) {
         // the mirror tile, read column-wise with two ds_read_b64_tr_b16 per
         // lane: in each 16-lane group G, lane s = 4 e + q points at row
         // IB + 32 G + 8 q + e (then + 4) of the 4-column chunk JB, so lane
         // 4 q + c receives rows IB + 32 G + 8 q .. +7 of column JB + c and
         // stores them as 16 bytes of mirror row JB + c; the 16 lanes with the
         // same c cover 128 consecutive entries (two cache lines) of that row.
+        // A diagonal tile is its own mirror: only the 32 x 32 blocks below its
+        // diagonal are written, from the computed blocks above it.
         bf16* mbase = out + d.a_off + (int64_t)j0 * d.m_pad + i0;
         const int G = lane >> 4, sl = lane & 15;
         const int sup_row = 32 * G + 8 * (sl & 3) + (sl >> 2);
@@ -508,7 +568,8 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             const bf16x4 lo = tr_read(smem + (IB + sup_row) * EROW + 2 * JB);
             const bf16x4 up = tr_read(smem + (IB + sup_row + 4) * EROW + 2 * JB);
             const bf16x8 v = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-            *reinterpret_cast<bf16x8*>(mbase + (int64_t)(JB + rc) * d.m_pad + IB + 32 * G + 8 * rq) = v;
+            if (!same || ((JB + rc) >> 5) > ((IB + 32 * G + 8 * rq) >> 5))
+                *reinterpret_cast<bf16x8*>(mbase + (int64_t)(JB + rc) * d.m_pad + IB + 32 * G + 8 * rq) = v;
         }
     }
 
