@@ -289,8 +289,11 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
             if (group_of[mi] != grp) continue;
             const int tm = d.m_pad / T, tn = d.n_pad / T;
             std::vector<TileWork> gl, ul;
+            // the matrix's upper tiles, the diagonal ones last: they compute
+            // only their blocks on or above the diagonal, about half a tile
             for (int ti = 0; ti < tm; ++ti)
-                for (int tj = ti; tj < tm; ++tj) gl.push_back({mi, (int16_t)ti, (int16_t)tj});
+                for (int tj = ti + 1; tj < tm; ++tj) gl.push_back({mi, (int16_t)ti, (int16_t)tj});
+            for (int ti = 0; ti < tm; ++ti) gl.push_back({mi, (int16_t)ti, (int16_t)ti});
             for (int ti = 0; ti < tm; ++ti)
                 for (int tj = 0; tj < tn; ++tj) ul.push_back({mi, (int16_t)ti, (int16_t)tj});
             g.push_back(gl);
