@@ -160,7 +160,9 @@ const char* muon_last_error(const muon_handle* h);
 /* Where matrix `index` (0-based over the table with counts expanded) lives
  * in the workspace: short-side shape m <= n, row stride ld (elements) of the
  * padded canonical buffers, element offsets into the X buffers and into the
- * per-row NorMuon arrays, transposed = stored rows > cols, active = !frozen. */
+ * per-row NorMuon arrays, transposed = stored rows > cols, active = !frozen,
+ * gram_offset = element offset of its m_pad x m_pad Gram / polynomial
+ * buffers (MUON_VIEW_GRAM / MUON_VIEW_POLY; -1 if frozen). */
 typedef struct muon_layout {
     int64_t x_offset;
     int64_t row_offset;
@@ -169,6 +171,7 @@ typedef struct muon_layout {
     int32_t active;
     int32_t stored_rows, stored_cols;
     int64_t param_offset;
+    int64_t gram_offset;
 } muon_layout;
 
 muon_status muon_matrix_layout(const muon_handle* h, int32_t index, muon_layout* out);
@@ -183,7 +186,10 @@ enum {
     MUON_VIEW_SCALE = 3,   /* float32 [num_matrices]: s = 1/(sqrt(sumsq) + ns_eps) */
     MUON_VIEW_V = 4,       /* float32 per canonical row: NorMuon second moment */
     MUON_VIEW_F = 5,       /* float32 per canonical row: NorMuon row factor */
-    MUON_VIEW_STATUS = 6   /* int32 [num_matrices]: bit 0 = non-finite u seen this step */
+    MUON_VIEW_STATUS = 6,  /* int32 [num_matrices]: bit 0 = non-finite u seen this step */
+    MUON_VIEW_GRAM = 7,    /* the last iteration's A = X X^T: m_pad x m_pad per matrix at its gram_offset
+                              (tiled matrices; the one-workgroup path keeps A in LDS, its region is unspecified) */
+    MUON_VIEW_POLY = 8     /* the last iteration's B' = a I + b A + c A A, same layout as MUON_VIEW_GRAM */
 };
 
 /* Device pointer and byte size of an internal buffer, valid after the

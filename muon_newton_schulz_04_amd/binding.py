@@ -37,6 +37,8 @@ MUON_VIEW_SCALE = 3
 MUON_VIEW_V = 4
 MUON_VIEW_F = 5
 MUON_VIEW_STATUS = 6
+MUON_VIEW_GRAM = 7
+MUON_VIEW_POLY = 8
 
 MUON_KERNEL_MOMENTUM = 0
 MUON_KERNEL_GRAM = 1
@@ -92,6 +94,7 @@ class muon_layout(ctypes.Structure):
         ("stored_rows", ctypes.c_int32),
         ("stored_cols", ctypes.c_int32),
         ("param_offset", ctypes.c_int64),
+        ("gram_offset", ctypes.c_int64),
     ]
 
 

@@ -432,6 +432,7 @@ muon_status muon_matrix_layout(const muon_handle* h, int32_t index, muon_layout*
     out->stored_rows = d.R;
     out->stored_cols = d.C;
     out->param_offset = d.p_off;
+    out->gram_offset = h->plan.active_flag[index] ? d.a_off : -1;
     return MUON_OK;
 }
 
@@ -447,6 +448,8 @@ muon_status muon_debug_view(const muon_handle* h, int32_t which, void** dev_ptr,
         case MUON_VIEW_V: *dev_ptr = h->ws + P.off_v; *bytes = (size_t)P.rows_total * 4; break;
         case MUON_VIEW_F: *dev_ptr = h->ws + P.off_f; *bytes = (size_t)P.rows_total * 4; break;
         case MUON_VIEW_STATUS: *dev_ptr = h->ws + P.off_status; *bytes = nm * 4; break;
+        case MUON_VIEW_GRAM: *dev_ptr = h->ws + P.off_a; *bytes = (size_t)P.a_elems * P.esize; break;
+        case MUON_VIEW_POLY: *dev_ptr = h->ws + P.off_b; *bytes = (size_t)P.a_elems * P.esize; break;
         default: return MUON_E_INVALID_ARG;
     }
     return MUON_OK;

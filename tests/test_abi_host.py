@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 def test_struct_sizes_match_c_layout():
     assert ctypes.sizeof(B.muon_matrix) == 48
     assert ctypes.sizeof(B.muon_hparams) == 4 * 4 + 16 * 3 * 4 + 4 * 7
-    assert ctypes.sizeof(B.muon_layout) == 8 + 8 + 8 * 4 + 8
+    assert ctypes.sizeof(B.muon_layout) == 8 + 8 + 8 * 4 + 8 + 8
 
 
 def test_hparams_default_values():

@@ -143,6 +143,42 @@ def test_step_captured_in_a_hip_graph_replays_like_eager():
         assert torch.equal(run.mom, eager_m), f"replay {r}: momentum differs from the eager step"
 
 
+def test_gram_and_polynomial_buffers_are_symmetric_and_consistent():
+    # The large-tile kernels compute only upper tiles, and on a diagonal tile
+    # only the 32 x 32 blocks on or above its diagonal; everything below is
+    # written from the mirror image. So the last iteration's A and B' must be
+    # exactly symmetric, and B' must be the bf16 polynomial a I + b A + c A A
+    # of that A (fp64 here, fp32 accumulation on the GPU).
+    shapes = [(768, 768, 2, "spike"), (768, 3072, 1, "spike"), (3072, 768, 1, "gauss"),
+              (300, 200, 1, "spike"), (200, 260, 1, "gauss"), (64, 64, 2, "rank8")]
+    w = custom_workload(112, shapes, steps=1, lr=0.02)
+    run = GpuRun(w)
+    run.load_grads(0)
+    run.step()
+    A_all = run.H.view(B.MUON_VIEW_GRAM, torch.bfloat16)
+    P_all = run.H.view(B.MUON_VIEW_POLY, torch.bfloat16)
+    a, b, c = O.default_coeffs()[-1]
+    checked = set()
+    for gi, *_ in run.subs:
+        L = run.lay[gi]
+        if L.m_pad == 64 and L.ld <= 512:
+            continue  # one-workgroup path: A and B' stay in LDS
+        sz = L.m_pad * L.m_pad
+        A = A_all[L.gram_offset:L.gram_offset + sz].view(L.m_pad, L.m_pad)
+        P = P_all[L.gram_offset:L.gram_offset + sz].view(L.m_pad, L.m_pad)
+        assert torch.equal(A, A.t().contiguous()), f"A of matrix {gi} not symmetric"
+        assert torch.equal(P, P.t().contiguous()), f"B' of matrix {gi} not symmetric"
+        An = A.float().cpu().numpy().astype(np.float64)[:L.m, :L.m]
+        Pn = P.float().cpu().numpy().astype(np.float64)[:L.m, :L.m]
+        assert np.all(np.diag(An) >= 0)
+        ref = O.bf16_round(a * np.eye(L.m) + b * An + c * (An @ An))
+        err = np.linalg.norm(Pn - ref) / np.linalg.norm(ref)
+        _say(f"  matrix {gi} [{L.m} x {L.n}] m_pad {L.m_pad}: B' vs poly(A) {err:.2e}")
+        assert err <= 5e-3
+        checked.add(L.m_pad)
+    assert {256, 768} <= checked  # one- and three-tile diagonals covered
+
+
 def test_weight_decay_large_tiles_ragged():
     w = custom_workload(109, LARGE_TILES, steps=3, lr=0.05, weight_decay=0.1)
     _run_all_stages(w, 3)
