@@ -468,9 +468,31 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         return smem + ((nk + il / ARPB_E) % NBUF) * LY::STAGE + (il % ARPB_E) * LY::XROWB + 8 * hi;
     };
     const int asw = l32 & 15;
+    // the A entries of one 32-row block (8 loads), read a block ahead of their
+    // use so the LDS latency is paid once per block, not once per load
+    uint2 a_cur[FRJ][4], a_nxt[FRJ][4];
+    auto read_a = [&](int fi, uint2 (&dst)[FRJ][4]) {
+        if constexpr (MODE == NS_POLY) {
+            const char* row = abase(wi * WTM + fi * 32 + l32);
+#pragma unroll
+            for (int fj = 0; fj < FRJ; ++fj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    dst[fj][g] = *reinterpret_cast<const uint2*>(row + 16 * ((4 * colblk(fj) + g) ^ asw));
+        }
+    };
+    read_a(0, a_nxt);
 #pragma unroll
     for (int fi = 0; fi < FRI; ++fi) {
         const int il = wi * WTM + fi * 32 + l32;
+        if constexpr (MODE == NS_POLY) {
+#pragma unroll
+            for (int fj = 0; fj < FRJ; ++fj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) a_cur[fj][g] = a_nxt[fj][g];
+            if (fi + 1 < FRI) read_a(fi + 1, a_nxt);
+            __builtin_amdgcn_sched_barrier(0);  // the next block's loads go out first
+        }
 #pragma unroll
         for (int fj = 0; fj < FRJ; ++fj) {
 #pragma unroll
@@ -481,9 +503,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
                 for (int e = 0; e < 4; ++e) v[e] = acc[fi][fj][4 * g + e];
                 if (MODE == NS_POLY) {
                     // P = a I + b A + c A A: the a X term of the update rides on P's diagonal
-                    const int c = 4 * colblk(fj) + g;
-                    const uint2 in =
-                        *reinterpret_cast<const uint2*>(abase(il) + 16 * (c ^ asw));
+                    const uint2 in = a_cur[fj][g];
                     v[0] = fmaf(cb, bf16_lo(in.x), cc * v[0]);
                     v[1] = fmaf(cb, bf16_hi(in.x), cc * v[1]);
                     v[2] = fmaf(cb, bf16_lo(in.y), cc * v[2]);
