@@ -105,6 +105,15 @@ constexpr unsigned diag_mask(int wi, int wj, int WN, int FRI) {
         }
     return m;
 }
+// The blocks of a wave on an edge tile: row blocks fi < RV, column block
+// fj = 0 if CM >= 1 and fj = 1 if CM == 2 (same bit order as diag_mask).
+constexpr unsigned edge_mask(int RV, int CM, int FRI) {
+    unsigned m = 0;
+    for (int fi = 0; fi < RV && fi < FRI; ++fi)
+        for (int fj = 0; fj < 2; ++fj)
+            if (CM > fj) m |= 1u << (fi * 2 + fj);
+    return m;
+}
 constexpr int bit_count(unsigned m) { return m ? (int)(m & 1u) + bit_count(m >> 1) : 0; }
 // the position of the k-th set bit of m
 constexpr int nth_bit(unsigned m, int k) {
@@ -182,22 +191,25 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     const bf16* Psrc;
     const bf16* Qsrc;
     int ldp, ldq, K;
+    // K stops at the first BK slice that lies wholly in the zero padding:
+    // the padded columns of X (Gram) and of A (polynomial, update) are zero,
+    // so the trimmed sum is the full one
     if (MODE == NS_GRAM) {
         Psrc = xin + d.x_off + (int64_t)i0 * d.n_pad;
         Qsrc = xin + d.x_off + (int64_t)j0 * d.n_pad;
         ldp = ldq = d.n_pad;
-        K = d.n_pad;
+        K = (d.n + BK - 1) / BK * BK;
     } else if (MODE == NS_POLY) {
         Psrc = ain + d.a_off + (int64_t)i0 * d.m_pad;
         Qsrc = ain + d.a_off + (int64_t)j0 * d.m_pad;
         ldp = ldq = d.m_pad;
-        K = d.m_pad;
+        K = (d.m + BK - 1) / BK * BK;
     } else {
         Psrc = ain + d.a_off + (int64_t)i0 * d.m_pad;  // rows of B
         Qsrc = xin + d.x_off + j0;                     // columns j0.. of X; row k = contraction
         ldp = d.m_pad;
         ldq = d.n_pad;
-        K = d.m_pad;
+        K = (d.m + BK - 1) / BK * BK;
     }
     // buffer ranges: the tile's rows (P, and Q for Gram / poly) or all K rows of X
     const __amdgpu_buffer_rsrc_t rp = rsrc(Psrc, (uint32_t)(T * ldp * 2));
@@ -393,7 +405,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         }
     };
 
-    const int nk = K / BK;  // >= 2 (K >= 128)
+    const int nk = K / BK;  // >= 3 for the Gram (K >= 96), >= 2 otherwise (K >= 128): m > 64 here
     static_assert(D <= 4, "ring depth");
     auto buf = [&](int k) { return smem + (k % NBUF) * LY::STAGE; };
 #pragma unroll
@@ -415,7 +427,29 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     };
     constexpr unsigned FULL = (1u << (FRI * FRJ)) - 1;
     if (MODE == NS_UPDATE || !same) {
-        main_loop(std::integral_constant<unsigned, FULL>{});
+        // Edge tiles of padded matrices: output rows >= m and columns >= m
+        // (Gram, polynomial) or >= n (update) are zero (P there is a I, which
+        // the epilogue adds), so a wave skips its 32 x 32 blocks that lie
+        // wholly in the padding. RV: its row blocks below the edge; CM: 2 if
+        // both column blocks are inside, 1 if only block wj (the other,
+        // 2 WN - 1 - wj, is further right). All waves still run every stage's
+        // loads and barriers.
+        const int vcol = MODE == NS_UPDATE ? d.n : d.m;
+        const int rrem = d.m - (i0 + wi * WTM);
+        const int rv = rrem <= 0 ? 0 : rrem >= WTM ? FRI : (rrem + 31) / 32;
+        const int cm = j0 + 32 * cb1 < vcol ? 2 : j0 + 32 * wj < vcol ? 1 : 0;
+        if (rv == FRI && cm == 2) {
+            main_loop(std::integral_constant<unsigned, FULL>{});
+        } else {
+            static_for<0, FRI + 1>([&](auto r_c) {
+                constexpr int RV = decltype(r_c)::value;
+                static_for<0, 3>([&](auto c_c) {
+                    constexpr int CM = decltype(c_c)::value;
+                    if constexpr (!(RV == FRI && CM == 2))
+                        if (rv == RV && cm == CM) main_loop(std::integral_constant<unsigned, edge_mask(RV, CM, FRI)>{});
+                });
+            });
+        }
     } else {
         // a diagonal tile: each wave type runs its own fixed block list
         static_for<0, NWV>([&](auto w_c) {

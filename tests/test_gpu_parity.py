@@ -95,6 +95,8 @@ LARGE_TILES = [
     (96, 160, 1, "gauss", 1.0, 1),        # frozen
     (65, 131, 1, "student_t", 0.0),       # lr_mul 0
     (129, 67, 2, "gauss"),                # odd widths: scalar edge path
+    (300, 560, 1, "spike"),               # 128-tiles: last tile row leaves a wave's rows all padding
+    (1100, 420, 1, "spike"),              # 256-tiles, transposed: edge waves with 0, 1 or 2 column blocks
 ]
 
 
