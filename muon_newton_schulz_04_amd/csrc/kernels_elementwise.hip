@@ -122,8 +122,55 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MatDesc* __restrict
     const int cg = (tid & 15) * 4;
     const int rg = tid >> 4;
     float ssq = 0.0f;
+    // interior tile with 16-byte aligned rows: all four passes' loads go out
+    // before the first is used (the general path below waits pass by pass)
+    const bool interior = d.vec_ok && tc.i0 + TS <= d.m && tc.j0 + TS <= d.n;
 
-    if (!d.transposed) {
+    if (interior) {
+        // canonical (i, j) is stored (i, j), or (j, i) when transposed; the
+        // stored-frame rows r0 + rg + 16 p, columns c0 + cg .. +3 are read
+        const int r0 = d.transposed ? tc.j0 : tc.i0;
+        const int c0 = d.transposed ? tc.i0 : tc.j0;
+        float4 g4[4], m4[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int64_t base = d.p_off + (int64_t)(r0 + rg + 16 * p) * d.C + c0 + cg;
+            g4[p] = ntld4(grads + base);
+            m4[p] = ntld4(mom + base);
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            float u[4];
+            u[0] = mom_update(g4[p].x, m4[p].x, P);
+            u[1] = mom_update(g4[p].y, m4[p].y, P);
+            u[2] = mom_update(g4[p].z, m4[p].z, P);
+            u[3] = mom_update(g4[p].w, m4[p].w, P);
+            ntst4(mom + d.p_off + (int64_t)(r0 + rg + 16 * p) * d.C + c0 + cg, m4[p]);
+            if (!d.transposed) {
+                ssq = fmaf(u[0], u[0], ssq);
+                ssq = fmaf(u[1], u[1], ssq);
+                ssq = fmaf(u[2], u[2], ssq);
+                ssq = fmaf(u[3], u[3], ssq);
+                store_x4<XT>(xt + d.x_off + (int64_t)(tc.i0 + rg + 16 * p) * d.n_pad + tc.j0 + cg, u[0], u[1], u[2],
+                             u[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ssq = fmaf(u[e], u[e], ssq);
+                    lds[cg + e][rg + 16 * p] = u[e];
+                }
+            }
+        }
+        if (d.transposed) {
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int il = rg + 16 * p;
+                store_x4<XT>(xt + d.x_off + (int64_t)(tc.i0 + il) * d.n_pad + tc.j0 + cg, lds[il][cg],
+                             lds[il][cg + 1], lds[il][cg + 2], lds[il][cg + 3]);
+            }
+        }
+    } else if (!d.transposed) {
         // canonical (i, j) == stored (i, j)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -228,7 +275,57 @@ __global__ __launch_bounds__(kThreads) void k_apply(const MatDesc* __restrict__ 
     const float decay = 1.0f - lrm * wd * d.wd_mul;
     const float coef0 = lrm * d.shape_scale;
 
-    if (!d.transposed) {
+    if (d.vec_ok && tc.i0 + TS <= d.m && tc.j0 + TS <= d.n) {
+        // interior tile with 16-byte aligned rows: every load of the tile
+        // goes out before the first is used
+        float x[4][4];
+        float4 p4[4];
+        const int r0 = d.transposed ? tc.j0 : tc.i0;
+        const int c0 = d.transposed ? tc.i0 : tc.j0;
+        // NorMuon row factors: of the canonical rows i0 + rg + 16 p, or (transposed)
+        // of the canonical rows i0 + cg + e that are this thread's stored columns
+        float fv[4] = {1.f, 1.f, 1.f, 1.f};
+        if (fr) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) fv[q] = fr[d.row_off + tc.i0 + (d.transposed ? cg + q : rg + 16 * q)];
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            load_x4<XT>(xo + d.x_off + (int64_t)(tc.i0 + rg + 16 * p) * d.n_pad + tc.j0 + cg, x[p]);
+            p4[p] = ntld4(params + d.p_off + (int64_t)(r0 + rg + 16 * p) * d.C + c0 + cg);
+        }
+        if (!d.transposed) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int i = tc.i0 + rg + 16 * p;
+                const float coef = fr ? coef0 * fv[p] : coef0;
+                p4[p].x = fmaf(-coef, x[p][0], p4[p].x * decay);
+                p4[p].y = fmaf(-coef, x[p][1], p4[p].y * decay);
+                p4[p].z = fmaf(-coef, x[p][2], p4[p].z * decay);
+                p4[p].w = fmaf(-coef, x[p][3], p4[p].w * decay);
+                ntst4(params + d.p_off + (int64_t)i * d.C + tc.j0 + cg, p4[p]);
+            }
+        } else {
+            // O rows (canonical) through LDS to stored rows
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lds[cg + e][rg + 16 * p] = x[p][e];
+            float coef[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) coef[e] = fr ? coef0 * fv[e] : coef0;
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int rl = rg + 16 * p;
+                p4[p].x = fmaf(-coef[0], lds[rl][cg], p4[p].x * decay);
+                p4[p].y = fmaf(-coef[1], lds[rl][cg + 1], p4[p].y * decay);
+                p4[p].z = fmaf(-coef[2], lds[rl][cg + 2], p4[p].z * decay);
+                p4[p].w = fmaf(-coef[3], lds[rl][cg + 3], p4[p].w * decay);
+                ntst4(params + d.p_off + (int64_t)(tc.j0 + rl) * d.C + tc.i0 + cg, p4[p]);
+            }
+        }
+    } else if (!d.transposed) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int i = tc.i0 + rg + 16 * p;
