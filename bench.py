@@ -163,9 +163,9 @@ def mfma_summary(pmc_dir: str, workload_id: int) -> dict:
     out = {"workload": w.name, "source_hash": _kernel_source_hash(),
            "commands": ["cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc MfmaUtil "
                         "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d "
-                        "$REPO/gpurun_out/pmc_mfma2 -o run -- python3 $REPO/bench.py --steps 3 --warmup 1 "
+                        "$REPO/gpurun_out/pmc_mfma -o run -- python3 $REPO/bench.py --steps 3 --warmup 1 "
                         "--no-cpu-baseline",
-                        "python3 bench.py --pmc-mfma-summary gpurun_out/pmc_mfma2"],
+                        "python3 bench.py --pmc-mfma-summary gpurun_out/pmc_mfma"],
            "note": "mfma_util_pct is rocprofiler's MfmaUtil (sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (max over "
                    "the XCDs of GRBM_GUI_ACTIVE x SIMDs) x 100); executed_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; "
                    "alg_flop counts the symmetric Gram and A A as m(m+1)k, so executed / alg > 1 is the diagonal "
