@@ -25,14 +25,16 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 bool finite(float x) { return std::isfinite(x); }
 
-// GEMM tile for a matrix whose short side is m: 256 (bf16 only) unless it
-// pads m by more than m / 8 beyond what 128 would, 128 for medium, 64 small.
-// The 256-tile kernel (8 waves, 2 per SIMD) moves half the bytes per flop of
-// the 128-tile one (4 waves): for m = 1600 it wins at m_pad 1792 against 1664
-// (1.5B body: 57.3 against 63.1 ms per step).
+// GEMM tile for a matrix whose short side is m: 256 (bf16 only, m >= 256)
+// unless it pads m by more than m / 8 beyond what 128 would, 128 for medium,
+// 64 small. The 256-tile kernel (8 waves, 2 per SIMD) moves half the bytes
+// per flop of the 128-tile one (4 waves): for m = 1600 it wins at m_pad 1792
+// against 1664 (1.5B body: 57.3 against 63.1 ms per step), and at m = 256
+// (256 x 1024 matrices) its one diagonal Gram tile beats three 128-tiles
+// (32 against 38 us per launch for 192 matrices).
 int pick_tile(int64_t m, bool fp32) {
     if (m <= 64) return 64;
-    if (!fp32 && m >= 384 && round_up(m, 256) <= round_up(m, 128) + m / 8) return 256;
+    if (!fp32 && m >= 256 && round_up(m, 256) <= round_up(m, 128) + m / 8) return 256;
     return 128;
 }
 

@@ -151,8 +151,12 @@ def test_gram_and_polynomial_buffers_are_symmetric_and_consistent():
     # written from the mirror image. So the last iteration's A and B' must be
     # exactly symmetric, and B' must be the bf16 polynomial a I + b A + c A A
     # of that A (fp64 here, fp32 accumulation on the GPU).
+    # Padded edges (700 -> 768 on 256-tiles, 200 / 300 -> 256 on 128-tiles)
+    # must hold A = 0 and B' = a I there: edge waves skip the blocks that lie
+    # wholly in the padding, so those values come from the epilogue alone.
     shapes = [(768, 768, 2, "spike"), (768, 3072, 1, "spike"), (3072, 768, 1, "gauss"),
-              (300, 200, 1, "spike"), (200, 260, 1, "gauss"), (64, 64, 2, "rank8")]
+              (300, 200, 1, "spike"), (200, 260, 1, "gauss"), (64, 64, 2, "rank8"),
+              (1000, 700, 1, "spike"), (256, 1024, 1, "spike")]
     w = custom_workload(112, shapes, steps=1, lr=0.02)
     run = GpuRun(w)
     run.load_grads(0)
@@ -170,8 +174,13 @@ def test_gram_and_polynomial_buffers_are_symmetric_and_consistent():
         P = P_all[L.gram_offset:L.gram_offset + sz].view(L.m_pad, L.m_pad)
         assert torch.equal(A, A.t().contiguous()), f"A of matrix {gi} not symmetric"
         assert torch.equal(P, P.t().contiguous()), f"B' of matrix {gi} not symmetric"
-        An = A.float().cpu().numpy().astype(np.float64)[:L.m, :L.m]
-        Pn = P.float().cpu().numpy().astype(np.float64)[:L.m, :L.m]
+        Af = A.float().cpu().numpy().astype(np.float64)
+        Pf = P.float().cpu().numpy().astype(np.float64)
+        pad_a = O.bf16_round(np.float64(a)) * np.eye(L.m_pad - L.m)
+        assert np.all(Af[L.m:, :] == 0) and np.all(Pf[L.m:, :L.m] == 0), f"matrix {gi}: padding not zero"
+        assert np.array_equal(Pf[L.m:, L.m:], pad_a), f"matrix {gi}: B' padding is not a I"
+        An = Af[:L.m, :L.m]
+        Pn = Pf[:L.m, :L.m]
         assert np.all(np.diag(An) >= 0)
         ref = O.bf16_round(a * np.eye(L.m) + b * An + c * (An @ An))
         err = np.linalg.norm(Pn - ref) / np.linalg.norm(ref)
