@@ -31,9 +31,12 @@ bool finite(float x) { return std::isfinite(x); }
 // per flop of the 128-tile one (4 waves): for m = 1600 it wins at m_pad 1792
 // against 1664 (1.5B body: 57.3 against 63.1 ms per step), and at m = 256
 // (256 x 1024 matrices) its one diagonal Gram tile beats three 128-tiles
-// (32 against 38 us per launch for 192 matrices).
+// (32 against 38 us per launch for 192 matrices). fp32 matrices up to
+// m = 256 take 64-tiles: the fp32 MFMA rate per CU is a sixteenth of bf16,
+// so spreading a small matrix over more workgroups pays (tiny d = 128 body:
+// one 128-tile per Gram took 62 us).
 int pick_tile(int64_t m, bool fp32) {
-    if (m <= 64) return 64;
+    if (m <= 64 || (fp32 && m <= 256)) return 64;
     if (!fp32 && m >= 256 && round_up(m, 256) <= round_up(m, 128) + m / 8) return 256;
     return 128;
 }
