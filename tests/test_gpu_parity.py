@@ -97,6 +97,7 @@ LARGE_TILES = [
     (129, 67, 2, "gauss"),                # odd widths: scalar edge path
     (300, 560, 1, "spike"),               # 128-tiles: last tile row leaves a wave's rows all padding
     (1100, 420, 1, "spike"),              # 256-tiles, transposed: edge waves with 0, 1 or 2 column blocks
+    (300, 2100, 1, "spike"),              # K >= 2048: Gram tiles split in two K halves
 ]
 
 
