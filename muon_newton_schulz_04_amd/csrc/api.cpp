@@ -231,6 +231,9 @@ muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, co
     }
     if (e == hipSuccess && P.rows_total) e = hipMemset(h->ws + P.off_v, 0, (size_t)P.rows_total * 4);
     if (e == hipSuccess && P.mats.size()) e = hipMemset(h->ws + P.off_status, 0, P.mats.size() * 4);
+    // the momentum kernel writes X~ only over the valid block rounded up to
+    // 64 x 64 tiles; the rest of the padding stays as zeroed here
+    if (e == hipSuccess && P.x_elems) e = hipMemset(h->ws + P.off_xt, 0, (size_t)P.x_elems * P.esize);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (prev >= 0) (void)hipSetDevice(prev);
     if (e != hipSuccess) {

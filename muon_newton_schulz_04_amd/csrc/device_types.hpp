@@ -32,7 +32,7 @@ struct MatDesc {
     int32_t row_off;      // offset into the per-row NorMuon arrays (v, f)
     int32_t ew_start;     // first elementwise tile (index into the momentum partials)
     int32_t ew_count;     // number of elementwise tiles
-    int32_t ew_tiles_n;   // elementwise tiles per canonical row band (n_pad / 64)
+    int32_t ew_tiles_n;   // elementwise tiles per canonical row band (ceil(n / 64))
     float lr_mul, wd_mul, shape_scale;
     int32_t vec_ok;       // stored rows start 16-byte aligned (float4 access legal)
 };

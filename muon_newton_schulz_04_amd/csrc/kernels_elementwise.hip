@@ -8,8 +8,10 @@
 // [P2] "2025-10-27_FixMuonLR" analysis, change 2 (lerp momentum buffer,
 // NorMuon per-lane second moment along the longer dimension).
 //
-// All kernels work on 64 x 64 tiles of a matrix's padded canonical frame
-// (rows <= cols). Matrices stored with rows > cols are transposed through
+// All kernels work on 64 x 64 tiles of a matrix's canonical frame (rows <=
+// cols), over its valid block rounded up to whole tiles; the momentum kernel
+// writes zeros into the padding inside those tiles (the rest of the X~
+// padding is zeroed once when the handle is created). Matrices stored with rows > cols are transposed through
 // LDS so that both the stored-frame and canonical-frame accesses stay
 // coalesced.
 

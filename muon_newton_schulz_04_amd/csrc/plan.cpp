@@ -210,8 +210,10 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
                 d.a_off = P.a_elems;
                 d.row_off = (int32_t)P.rows_total;
                 d.rowpart_off = nm ? P.rowpart_elems : 0;
-                d.ew_tiles_n = d.n_pad / kEwTile;
-                d.ew_count = (d.m_pad / kEwTile) * d.ew_tiles_n;
+                // elementwise tiles cover the valid block rounded up to 64: the
+                // X~ padding beyond it is zeroed once at init and never written
+                d.ew_tiles_n = (d.n + kEwTile - 1) / kEwTile;
+                d.ew_count = ((d.m + kEwTile - 1) / kEwTile) * d.ew_tiles_n;
                 d.ew_start = (int32_t)ew_tiles;
                 P.x_elems += (int64_t)d.m_pad * d.n_pad;
                 P.a_elems += (int64_t)d.m_pad * d.m_pad;
