@@ -71,6 +71,17 @@ def test_workspace_bytes_arithmetic():
     x32 = 128 * 320 * 4
     a32 = 128 * 128 * 4
     assert s2 == B.MUON_OK and nbytes32 >= 3 * x32 + 2 * a32
+    # tile choice: a small fp32 matrix goes on 64-tiles (136 x 520 -> 192 x 576,
+    # not 256 x 640 as 128-tiles would pad it); a bf16 256 x 1024 matrix is not
+    # padded at all
+    w2 = custom_workload(51, [(136, 520, 1)])
+    s4, nb4 = _ws(w2.entries, B.make_hparams(precision="fp32"))
+    assert s4 == B.MUON_OK
+    assert 3 * 192 * 576 * 4 + 2 * 192 * 192 * 4 <= nb4 < 3 * 256 * 640 * 4 + 2 * 256 * 256 * 4
+    w3 = custom_workload(52, [(256, 1024, 2)])
+    s5, nb5 = _ws(w3.entries, B.muon_hparams_default())
+    assert s5 == B.MUON_OK
+    assert 2 * (3 * 256 * 1024 * 2 + 2 * 256 * 256 * 2) <= nb5 < 2 * (3 * 384 * 1024 * 2 + 2 * 384 * 384 * 2)
     # the 124M body: 48 padded 768^2 + 24 padded 768 x 3072 canonical matrices
     body = get_workload(1)
     s3, nb = _ws(body.entries, B.muon_hparams_default())
