@@ -83,7 +83,15 @@ def _pmc_rows(d: str):
         yield from csv.DictReader(f)
 
 
-def pmc_summary(fetch_dir: str, write_dir: str, workload: str) -> dict:
+def _pmc_args(workload_id: int):
+    """Directory suffix, bench.py arguments and time limit (s) of the counter
+    runs for a workload (the 1.5B body's inputs take minutes to generate)."""
+    if workload_id == 1:
+        return "", "", 120
+    return f"_c{workload_id}", f" --config {workload_id}", 300
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str, workload_id: int = 1) -> dict:
     """Per-launch HBM traffic of each NS kernel class from two rocprofv3
     --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by
     what the same counter reads for the 1 GiB calibration copy."""
@@ -107,11 +115,12 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str) -> dict:
         per[counter] = {k: statistics.median(v[max(v)]) for k, v in vals.items()}
     fscale = COPY_BYTES / per["FETCH_SIZE"]["copy"]
     wscale = COPY_BYTES / per["WRITE_SIZE"]["copy"]
-    cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc {c} -f csv -d $REPO/gpurun_out/{d} "
-           "-o run -- python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
+    sfx, cfg, lim = _pmc_args(workload_id)
+    cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL " + str(lim) + " rocprofv3 --pmc {c} -f csv -d $REPO/gpurun_out/{d} "
+           "-o run -- python3 $REPO/bench.py" + cfg + " --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
     out = {"workload": workload, "source_hash": _kernel_source_hash(),
-           "commands": [cmd.format(c="FETCH_SIZE", d="pmc_fetch"), cmd.format(c="WRITE_SIZE", d="pmc_write"),
-                        "python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write"],
+           "commands": [cmd.format(c="FETCH_SIZE", d="pmc_fetch" + sfx), cmd.format(c="WRITE_SIZE", d="pmc_write" + sfx),
+                        f"python3 bench.py{cfg} --pmc-summary gpurun_out/pmc_fetch{sfx} gpurun_out/pmc_write{sfx}"],
            "note": "FETCH_SIZE/WRITE_SIZE are KiB per dispatch; each is scaled so that the 1 GiB calibration "
                    "read/write (torch.neg over 2^28 floats) counts 2^30 bytes; medians over the dispatches with "
                    "the largest grid of each kernel class (the one-stream kernel pass the roofline is timed on)",
@@ -160,12 +169,13 @@ def mfma_summary(pmc_dir: str, workload_id: int) -> dict:
             continue
         d = per.setdefault(key, {}).setdefault(int(r["Grid_Size"]), {})
         d.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    sfx, cfg, lim = _pmc_args(workload_id)
     out = {"workload": w.name, "source_hash": _kernel_source_hash(),
-           "commands": ["cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc MfmaUtil "
+           "commands": [f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL {lim} rocprofv3 --pmc MfmaUtil "
                         "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 -f csv -d "
-                        "$REPO/gpurun_out/pmc_mfma -o run -- python3 $REPO/bench.py --steps 3 --warmup 1 "
+                        f"$REPO/gpurun_out/pmc_mfma{sfx} -o run -- python3 $REPO/bench.py{cfg} --steps 3 --warmup 1 "
                         "--no-cpu-baseline",
-                        "python3 bench.py --pmc-mfma-summary gpurun_out/pmc_mfma"],
+                        f"python3 bench.py{cfg} --pmc-mfma-summary gpurun_out/pmc_mfma{sfx}"],
            "note": "mfma_util_pct is rocprofiler's MfmaUtil (sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (max over "
                    "the XCDs of GRBM_GUI_ACTIVE x SIMDs) x 100); executed_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; "
                    "alg_flop counts the symmetric Gram and A A as m(m+1)k, so executed / alg > 1 is the diagonal "
@@ -325,7 +335,7 @@ def main() -> int:
     if args.pmc_summary:
         from workloads import get_workload as _gw
         wname = _gw(args.config).name
-        t = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wname)
+        t = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wname, args.config)
         path = os.path.join(ROOT, "profiles", f"traffic_{wname}.json")
         with open(path, "w") as f:
             json.dump(t, f, indent=1)
