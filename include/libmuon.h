@@ -21,8 +21,8 @@
  *  - Ownership: the caller owns params, grads, momentum and the workspace.
  *    A handle owns only host memory. The library never allocates device
  *    memory; muon_init uploads its descriptor tables into the caller's
- *    workspace with a blocking copy; muon_step and muon_reset only enqueue
- *    work on `stream` and never synchronise.
+ *    workspace and zeroes its state there, blocking; muon_step and
+ *    muon_reset only enqueue work on `stream` and never synchronise.
  *  - Errors: every call returns a muon_status; nothing aborts or throws
  *    across the ABI. Validation happens before any HIP call. A kernel fault
  *    surfaces at the caller's next synchronisation. Handles are not
@@ -120,8 +120,11 @@ muon_status muon_workspace_bytes(const muon_matrix* table, int32_t n, const muon
  * matrices with rows > cols run transposed, [P4] Muon source; same-shape
  * matrices batched per launch, [P2] change 2), upload descriptors into
  * `workspace` (device, caller-owned, >= muon_workspace_bytes, 256-B aligned,
- * kept for the handle's lifetime) and zero the NorMuon state. `device` is
- * the HIP device index; it must be current in every later call.
+ * kept for the handle's lifetime and not written by the caller), and zero
+ * the NorMuon state and the Newton–Schulz input buffer (whose padding beyond
+ * the matrices' 64 x 64 tiles no step writes again). Blocking: returns after
+ * these copies and fills are done. `device` is the HIP device index; it must
+ * be current in every later call.
  * n = 0 is allowed (every step is then a no-op). On error *out is NULL. */
 muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp,
                       void* workspace, size_t ws_bytes, int32_t device);
