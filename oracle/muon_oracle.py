@@ -37,6 +37,14 @@ Readings where the pages are silent or garbled (each listed in the design doc):
   R7 Decoupled weight decay p <- p*(1 - lr*lr_mul*wd*wd_mul) - ...; the shape
      scale uses the stored [R, C].
   R8 Frozen matrices: params, momentum and v untouched.
+
+Parity unpinned (defined by this oracle alone, no page fixes them):
+  - apply_update with weight decay != 0: the pages run Muon with wd = 0 only,
+    so the decoupled form of R7 is a reading; with wd = 0 it is the pages'
+    p <- p - lr * scale * O, which the pins do fix.
+  - the NorMuon orientation for non-square matrices (R6): the pins fix the
+    norm preservation, the equal-lanes identity and the statistics along the
+    longer side, but "per row of the canonical frame" is a reading.
 """
 
 from __future__ import annotations
