@@ -395,27 +395,57 @@ __global__ __launch_bounds__(kThreads) void k_apply(const MatDesc* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// K5: NorMuon factors, one block per active matrix.
+// K5: NorMuon factors, one block of kNormThreads per active matrix.
 //   r_i = (1/n) sum_j O_ij^2   (row partials written by the last NS update)
 //   v_i <- beta2 v_i + (1 - beta2) r_i
 //   d_i = sqrt(v_i) + eps
 //   f_i = gamma / d_i, gamma = sqrt(sum_i r_i / sum_i r_i / d_i^2)  (keeps ||O||_F)
+// A matrix's rows (m <= 1024 for the bodies here) are spread over 1024
+// threads, so each thread's loads of its row partials go out together; the
+// two sums are reduced in a fixed order (deterministic).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_normuon(const MatDesc* __restrict__ mats,
-                                                      const int32_t* __restrict__ active,
-                                                      const float* __restrict__ rowpart,
-                                                      float* __restrict__ v, float* __restrict__ f,
-                                                      float beta2, float eps) {
-    __shared__ float red[4];
+constexpr int kNormThreads = 1024;
+
+// block-wide sums of (a, b) over kNormThreads threads, in a fixed order
+__device__ __forceinline__ float2 block_sum2_1024(float a, float b, float2* red /* >= 16 */) {
+    a = wave_sum(a);
+    b = wave_sum(b);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = make_float2(a, b);
+    __syncthreads();
+    float2 t = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kNormThreads / 64; ++w) {
+        t.x += red[w].x;
+        t.y += red[w].y;
+    }
+    return t;
+}
+
+__global__ __launch_bounds__(kNormThreads) void k_normuon(const MatDesc* __restrict__ mats,
+                                                          const int32_t* __restrict__ active,
+                                                          const float* __restrict__ rowpart,
+                                                          float* __restrict__ v, float* __restrict__ f,
+                                                          float beta2, float eps) {
+    __shared__ float2 red[kNormThreads / 64];
     const int mi = active[blockIdx.x];
     const MatDesc d = mats[mi];
     const int ntn = d.n_pad / d.T;
     const float inv_n = 1.0f / (float)d.n;
+    const float* rp = rowpart + d.rowpart_off;
     float s1 = 0.f, s2 = 0.f;
-    for (int i = threadIdx.x; i < d.m; i += kThreads) {
-        float r = 0.f;
-        for (int t = 0; t < ntn; ++t) r += rowpart[d.rowpart_off + (int64_t)t * d.m_pad + i];
-        r *= inv_n;
+    for (int i = threadIdx.x; i < d.m; i += kNormThreads) {
+        // four independent chains over the row's partials, summed in a fixed order
+        float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+        int t = 0;
+        for (; t + 4 <= ntn; t += 4) {
+            r0 += rp[(int64_t)t * d.m_pad + i];
+            r1 += rp[(int64_t)(t + 1) * d.m_pad + i];
+            r2 += rp[(int64_t)(t + 2) * d.m_pad + i];
+            r3 += rp[(int64_t)(t + 3) * d.m_pad + i];
+        }
+        for (; t < ntn; ++t) r0 += rp[(int64_t)t * d.m_pad + i];
+        const float r = ((r0 + r1) + (r2 + r3)) * inv_n;
         const float vi = fmaf(beta2, v[d.row_off + i], (1.0f - beta2) * r);
         v[d.row_off + i] = vi;
         const float di = sqrtf(vi) + eps;
@@ -423,11 +453,9 @@ __global__ __launch_bounds__(kThreads) void k_normuon(const MatDesc* __restrict_
         s2 += r / (di * di);
         f[d.row_off + i] = di;
     }
-    const float S1 = block_sum_256(s1, red);
-    __syncthreads();
-    const float S2 = block_sum_256(s2, red);
-    const float gamma = S2 > 0.f ? sqrtf(S1 / S2) : 0.f;
-    for (int i = threadIdx.x; i < d.m; i += kThreads) f[d.row_off + i] = gamma / f[d.row_off + i];
+    const float2 S = block_sum2_1024(s1, s2, red);
+    const float gamma = S.y > 0.f ? sqrtf(S.x / S.y) : 0.f;
+    for (int i = threadIdx.x; i < d.m; i += kNormThreads) f[d.row_off + i] = gamma / f[d.row_off + i];
 }
 
 // ---------------------------------------------------------------------------
@@ -495,7 +523,7 @@ hipError_t launch_apply(const LaunchCtx& L, const void* xo, const float* f, floa
 
 hipError_t launch_normuon(const LaunchCtx& L, float beta2, float eps) {
     if (L.n_active == 0) return hipSuccess;
-    k_normuon<<<L.n_active, kThreads, 0, L.stream>>>(L.mats, L.active, L.rowpart, L.v, L.f, beta2, eps);
+    k_normuon<<<L.n_active, kNormThreads, 0, L.stream>>>(L.mats, L.active, L.rowpart, L.v, L.f, beta2, eps);
     return hipGetLastError();
 }
 
