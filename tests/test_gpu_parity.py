@@ -253,6 +253,35 @@ def test_tiny_config_free_running_fp32():
         assert e_p <= 1e-6 and e_m <= 1e-6 and e_d <= 1e-4
 
 
+def test_per_call_schedules_free_running_fp32():
+    # The library's schedule functions drive every step through muon_step's
+    # per-call arguments: momentum warm-up 0.85 -> 0.95 over 4 steps
+    # (momentum_coef) and the WSD learning rate with a 3-step warm-down (lr),
+    # over 6 free-running fp32-NS steps on 64- and 128-tiles. Params and
+    # momentum vs the float64 oracle stepped with the same per-step values.
+    w = custom_workload(113, [(128, 128, 2, "gauss"), (96, 200, 1, "gauss"), (200, 96, 1, "gauss"),
+                              (300, 260, 1, "gauss")], steps=6, ns_precision="fp32")
+    run = GpuRun(w)
+    orc = O.OracleMuon(w.entries, w.total, momentum=w.momentum, mode="exact")
+    p0 = run.params.cpu().numpy().astype(np.float64)
+    p_or = p0.copy()
+    for t in range(6):
+        beta = B.muon_momentum_warmup(t, 4, 0.85, 0.95)
+        lr = 0.05 * B.muon_lr_wsd(t, 6, 0, 3)
+        g = run.load_grads(t)
+        p_or = orc.step(p_or, g, lr=lr, beta=beta)
+        run.step(lr=lr, momentum_coef=beta)
+    p = run.params.cpu().numpy().astype(np.float64)
+    m = run.mom.cpu().numpy().astype(np.float64)
+    for gi, _ei, _k, off, r, c in run.subs:
+        sl = slice(off, off + r * c)
+        e_p = O.rel_fro(p[sl], p_or[sl])
+        e_d = O.rel_fro(p[sl] - p0[sl], p_or[sl] - p0[sl])
+        e_m = O.rel_fro(m[sl], orc.m[sl])
+        _say(f"  matrix {gi} [{r} x {c}]: params {e_p:.2e} update {e_d:.2e} momentum {e_m:.2e}")
+        assert e_p <= 1e-6 and e_m <= 1e-6 and e_d <= 1e-4
+
+
 _P0 = {}
 
 
