@@ -101,6 +101,19 @@ LARGE_TILES = [
 ]
 
 
+def test_long_thin_matrices_all_stages():
+    # bf16 matrices whose short side is at most 64 but too long for the
+    # one-workgroup kernel (padded long side > 512) run on the generic 64-tile
+    # kernels, with K up to the whole long side: a single row of 2^20 (the
+    # dimension limit), tall and wide thin matrices, and a zero one
+    shapes = [(1, 1 << 20, 1, "gauss"), (3000, 20, 1, "spike"), (48, 1000, 2, "gauss"), (64, 700, 1, "rank8"),
+              (2, 5000, 1, "zero")]
+    w = custom_workload(114, shapes, steps=2, lr=0.05)
+    _run_all_stages(w, 2)
+    w2 = custom_workload(115, shapes[:3], steps=1, normuon=1, lr=0.05)
+    _run_all_stages(w2, 1)
+
+
 def test_stream_groups_give_identical_results():
     # the 9 tiled matrices split over 2, 3 or 4 streams, or all on the
     # caller's stream: the same kernels on the same tiles, so bit-identical
