@@ -5,6 +5,7 @@ inputs and compares every stage with the CPU oracle, per matrix:
   G1 momentum           (free-running)              rel. Frobenius <= 1e-6
   G2 X~ = bf16(u)        (u from the GPU's momentum)  within 1 bf16 ulp + fp32 blend error
   G3 Newton-Schulz      (given the GPU's X~ and s)  <= 2e-2 bf16 contract / 1e-4 fp32 vs exact;
+     beyond 5 iterations, bf16: <= max(2e-2, the contract's own distance from exact NS);
      for rank-deficient inputs (contract >5e-2 from exact NS) the 2e-2 gate
      applies to the dominant singular subspace, and the GPU must be no further
      from exact NS than 1.25x the contract's own distance + 2e-2
@@ -23,6 +24,13 @@ from workloads import gen_grads, gen_matrix_grad, gen_params
 TOL_MOM = 1e-6
 TOL_NS_BF16 = 2e-2
 TOL_NS_FP32 = 1e-4
+# The 2e-2 bf16 gate is stated for the five Newton-Schulz iterations of every
+# workload. The quintic does not converge (its singular values keep moving in
+# [0.68, 1.20]), so with more iterations two bf16 implementations with the
+# same rounding points but different accumulation orders drift further apart
+# each step; beyond five the GPU result must be no farther from the contract
+# than the contract is from exact NS (and the gate is never tighter than 2e-2).
+NS_STEPS_SPEC = 5
 TOL_PARAM = 1e-6
 TOL_DELTA = 1e-4  # the update p_new - p_old itself (float32 rounding of p bounds it)
 ILL_CONDITIONED = 5e-2  # bf16-contract vs exact NS above this: the input is rank-deficient
@@ -145,15 +153,16 @@ def check_stages(run: GpuRun, step: int, indices, grads_host=None, p_prev=None, 
         s_or = O.frobenius_scale(u)
         assert abs(s - s_or) <= 1e-5 * s_or + 1e-30, (gi, s, s_or)
         out = run.ns_out(gi)
+        co = O.default_coeffs(run.hp.ns_steps)  # the pages' coefficients, the run's step count
         if run.fp32:
-            ref_ns = O.ns_exact(xt, s)
+            ref_ns = O.ns_exact(xt, s, co)
         else:
-            ref_ns = O.ns_bf16_contract(xt, s)
+            ref_ns = O.ns_bf16_contract(xt, s, co)
         e3 = O.rel_fro(out, ref_ns)
         ce = 0.0
         if not run.fp32:
             # how far the bf16 method itself is from exact NS on this input
-            ex = O.ns_exact(xt, s)
+            ex = O.ns_exact(xt, s, co)
             ce = O.rel_fro(ref_ns, ex)
         if ce > ILL_CONDITIONED:
             # Rank-deficient input: outside the dominant singular subspace the
@@ -167,6 +176,8 @@ def check_stages(run: GpuRun, step: int, indices, grads_host=None, p_prev=None, 
             excess = O.rel_fro(out, ex) - (1.25 * ce + TOL_NS_BF16)
             worst["ns_ill_signal"] = max(worst.get("ns_ill_signal", 0.0), e_sig)
             worst["ns_ill_excess"] = max(worst.get("ns_ill_excess", -1.0), excess)
+        elif not run.fp32 and run.hp.ns_steps > NS_STEPS_SPEC:
+            worst["ns_long_excess"] = max(worst.get("ns_long_excess", -1.0), e3 - max(TOL_NS_BF16, ce))
         else:
             if e3 > worst["ns"]:
                 worst["ns_at"] = (gi, R, C, e.gclass)
@@ -194,6 +205,7 @@ def assert_worst(worst, fp32=False):
     assert worst["ns"] <= (TOL_NS_FP32 if fp32 else TOL_NS_BF16), worst
     assert worst.get("ns_ill_signal", 0.0) <= TOL_NS_BF16, worst
     assert worst.get("ns_ill_excess", -1.0) <= 0.0, worst
+    assert worst.get("ns_long_excess", -1.0) <= 0.0, worst
     assert worst["v"] <= TOL_MOM, worst
     assert worst["param"] <= TOL_PARAM, worst
     assert worst["delta"] <= TOL_DELTA, worst

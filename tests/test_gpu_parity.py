@@ -114,6 +114,16 @@ def test_long_thin_matrices_all_stages():
     _run_all_stages(w2, 1)
 
 
+@pytest.mark.parametrize("ns_steps", [1, 10, 16])
+def test_newton_schulz_step_counts(ns_steps):
+    # one iteration (the first is also the last: s scaling and the NorMuon row
+    # sums in the same update launch), the pages' signature default of 10 and
+    # the maximum of 16, on 256-, 128- and 64-tiles and the one-workgroup kernel
+    shapes = [(400, 520, 1, "spike"), (200, 300, 1, "spike"), (48, 1000, 1, "gauss"), (64, 64, 2, "gauss")]
+    w = custom_workload(116 + ns_steps, shapes, steps=2, normuon=1, ns_steps=ns_steps, lr=0.05)
+    _run_all_stages(w, 2)
+
+
 def test_stream_groups_give_identical_results():
     # the 9 tiled matrices split over 2, 3 or 4 streams, or all on the
     # caller's stream: the same kernels on the same tiles, so bit-identical
