@@ -97,7 +97,8 @@ LARGE_TILES = [
     (129, 67, 2, "gauss"),                # odd widths: scalar edge path
     (300, 560, 1, "spike"),               # 128-tiles: last tile row leaves a wave's rows all padding
     (1100, 420, 1, "spike"),              # 256-tiles, transposed: edge waves with 0, 1 or 2 column blocks
-    (300, 2100, 1, "spike"),              # K >= 2048: Gram tiles split in two K halves
+    (300, 2100, 1, "spike"),              # long K on 128-tiles
+    (700, 2100, 1, "spike"),              # long K on 256-tiles: Gram tiles in two column halves, padded edge
 ]
 
 
@@ -180,7 +181,7 @@ def test_gram_and_polynomial_buffers_are_symmetric_and_consistent():
     # wholly in the padding, so those values come from the epilogue alone.
     shapes = [(768, 768, 2, "spike"), (768, 3072, 1, "spike"), (3072, 768, 1, "gauss"),
               (300, 200, 1, "spike"), (200, 260, 1, "gauss"), (64, 64, 2, "rank8"),
-              (1000, 700, 1, "spike"), (256, 1024, 1, "spike")]
+              (1000, 700, 1, "spike"), (256, 1024, 1, "spike"), (2100, 700, 1, "spike")]
     w = custom_workload(112, shapes, steps=1, lr=0.02)
     run = GpuRun(w)
     run.load_grads(0)
