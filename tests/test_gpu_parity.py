@@ -98,7 +98,7 @@ LARGE_TILES = [
     (300, 560, 1, "spike"),               # 128-tiles: last tile row leaves a wave's rows all padding
     (1100, 420, 1, "spike"),              # 256-tiles, transposed: edge waves with 0, 1 or 2 column blocks
     (300, 2100, 1, "spike"),              # long K on 128-tiles
-    (700, 2100, 1, "spike"),              # long K on 256-tiles: Gram tiles in two column halves, padded edge
+    (700, 2100, 1, "spike"),              # long K on 256-tiles, padded edge
 ]
 
 
