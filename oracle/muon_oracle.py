@@ -29,8 +29,11 @@ Readings where the pages are silent or garbled (each listed in the design doc):
   R4 s = 1/(||u||_F + 1e-7) from the float u; in the bf16 rounding contract
      s is folded into iteration 0 instead of rounding s*X to bf16.
   R5 The bf16 rounding contract: the input X~ is rounded once, then three
-     rounding points per iteration (the bf16 outputs A, P = a I + b A + c A^2
-     and X = P X), each product accumulated exactly (float64 here).
+     rounding points per iteration, at the bf16 outputs of the three products
+     of the factored iteration: A = X X^T, B = b A + c A^2 and X = a X + B X.
+     Each product and sum is exact (float64 here); a X is added before the
+     rounding of the new X. The folded variant (a I carried inside the
+     rounded B) is kept beside it for comparison only.
   R6 NorMuon per row of the canonical (rows <= cols) frame: mean of squares
      over the longer dimension, v EMA with v0 = 0 and no bias correction,
      divide by sqrt(v)+eps, rescale to keep the Frobenius norm, 0/0 -> 0.
@@ -158,36 +161,45 @@ def ns_exact_factored(X, s: float, coeffs=None) -> np.ndarray:
 def ns_bf16_contract(Xt, s: float, coeffs=None) -> np.ndarray:
     """bf16 rounding contract of the factored iteration (readings R4, R5).
 
-    The quintic step X <- a X + b (X X^T) X + c (X X^T)^2 X is the matrix
-    polynomial (a I + b A + c A^2) applied to X, A = X X^T. Xt: the
-    bf16-rounded short-side input (float64 array of bf16 values); s: the
-    normalising factor, folded into iteration 0. Products are exact (float64);
-    R() rounds to bf16 at three points per iteration:
-      it 0:  A = R(s^2 Xt Xt^T);  P = R(a I + b A + c A A);  X = R(s P Xt)
-      it>0:  A = R(X X^T);        P = R(a I + b A + c A A);  X = R(P X)
+    [P4] Muon source: the loop A = X X^T, B = A X, X = a X + b B + c A B,
+    run in bf16. Grouping b A X + c A A X as (b A + c A^2) X gives the
+    factored step A = X X^T; B = b A + c A^2; X = a X + B X, whose three
+    products are the three rounding points here. Xt: the bf16-rounded
+    short-side input (float64 array of bf16 values); s: the normalising
+    factor, folded into iteration 0 (X = s Xt is never rounded itself).
+    Products and sums are exact (float64); R() rounds to bf16:
+      it 0:  A = R(s^2 Xt Xt^T);  B = R(b A + c A A);  X = R(a s Xt + s B Xt)
+      it>0:  A = R(X X^T);        B = R(b A + c A A);  X = R(a X + B X)
+    """
+    coeffs = default_coeffs() if coeffs is None else coeffs
+    X = np.asarray(Xt, np.float64)
+    for k, (a, b, c) in enumerate(coeffs):
+        g = (s * s) if k == 0 else 1.0      # iteration 0 sees s Xt
+        A = bf16_round(g * (X @ X.T))
+        Bm = bf16_round(b * A + c * (A @ A))
+        h = s if k == 0 else 1.0
+        X = bf16_round(h * (a * X + Bm @ X))
+    return X
+
+
+def ns_bf16_contract_folded(Xt, s: float, coeffs=None) -> np.ndarray:
+    """The same iteration with a I folded into the rounded polynomial:
+      A = R(g X X^T);  P = R(a I + b A + c A A);  X = R(h P X)
+    (g = s^2, h = s in iteration 0, else 1). Equal to ns_bf16_contract in
+    exact arithmetic; it rounds a + b A_ii + c (A A)_ii on the diagonal,
+    where the bf16 grid is coarse. Not a gate of the library; kept to
+    report how far the two placements of the a X term lie apart.
     """
     coeffs = default_coeffs() if coeffs is None else coeffs
     X = np.asarray(Xt, np.float64)
     eye = np.eye(X.shape[0])
     for k, (a, b, c) in enumerate(coeffs):
-        if k == 0:
-            A = bf16_round((s * s) * (X @ X.T))
-        else:
-            A = bf16_round(X @ X.T)
+        g = (s * s) if k == 0 else 1.0
+        A = bf16_round(g * (X @ X.T))
         P = bf16_round(a * eye + b * A + c * (A @ A))
-        if k == 0:
-            X = bf16_round(s * (P @ X))
-        else:
-            X = bf16_round(P @ X)
+        h = s if k == 0 else 1.0
+        X = bf16_round(h * (P @ X))
     return X
-
-
-def scalar_polynomial(x: float, coeffs=None) -> float:
-    """p(x) = a x + b x^3 + c x^5 composed once per iteration (for pins)."""
-    coeffs = default_coeffs() if coeffs is None else coeffs
-    for a, b, c in coeffs:
-        x = a * x + b * x ** 3 + c * x ** 5
-    return x
 
 
 # ----------------------------------------------------------------------------
@@ -329,5 +341,5 @@ __all__ = [
     "bf16_round", "bf16_ulp",
     "momentum_lerp", "nesterov_lerp", "momentum_heavy_ball", "nesterov_heavy_ball",
     "to_short_side", "frobenius_scale", "ns_exact", "ns_exact_factored", "ns_bf16_contract",
-    "scalar_polynomial", "normuon", "shape_scale", "apply_update", "OracleMuon", "rel_fro",
+    "ns_bf16_contract_folded", "normuon", "shape_scale", "apply_update", "OracleMuon", "rel_fro",
 ]

@@ -166,29 +166,109 @@ def test_bf16_contract_diagonal_recurrence():
     xt = O.bf16_round(u)
     s = 1.0 / (np.linalg.norm(u) + 1e-7)
     out = O.ns_bf16_contract(xt, s)
+    fold = O.ns_bf16_contract_folded(xt, s)
     a, b, c = 3.4445, -4.7750, 2.0315
     for i in range(m):
-        x = float(xt[i, i])
+        x = y = float(xt[i, i])
         for k in range(5):
-            A = _bf16_torch((s * s) * (x * x)) if k == 0 else _bf16_torch(x * x)
-            P = _bf16_torch(a + b * A + c * (A * A))
-            x = _bf16_torch(s * (P * x)) if k == 0 else _bf16_torch(P * x)
+            g = s * s if k == 0 else 1.0
+            h = s if k == 0 else 1.0
+            # four-point: A, B = b A + c A^2, X = a X + B X
+            A = _bf16_torch(g * (x * x))
+            Bv = _bf16_torch(b * A + c * (A * A))
+            x = _bf16_torch(h * (a * x + Bv * x))
+            # folded: P = a + b A + c A^2 rounded, X = P X
+            Ay = _bf16_torch(g * (y * y))
+            P = _bf16_torch(a + b * Ay + c * (Ay * Ay))
+            y = _bf16_torch(h * (P * y))
         assert abs(out[i, i] - x) <= O.bf16_ulp(x), (i, out[i, i], x)
-    off = out.copy()
-    off[np.arange(m), np.arange(m)] = 0
-    assert np.all(off == 0)
+        assert abs(fold[i, i] - y) <= O.bf16_ulp(y), (i, fold[i, i], y)
+    for r in (out, fold):
+        off = r.copy()
+        off[np.arange(m), np.arange(m)] = 0
+        assert np.all(off == 0)
+
+
+def _contract_scalar(Xt, s, steps=5, a=3.4445, b=-4.7750, c=2.0315):
+    # The four-point contract written with Python loops over entries and torch's
+    # float64 -> bfloat16 cast at each rounding point (independent of the
+    # oracle's matrix code and of its rounding routine).
+    m, n = len(Xt), len(Xt[0])
+    X = [list(map(float, row)) for row in Xt]
+    for k in range(steps):
+        g = s * s if k == 0 else 1.0
+        h = s if k == 0 else 1.0
+        A = [[_bf16_torch(g * sum(X[i][t] * X[j][t] for t in range(n))) for j in range(m)] for i in range(m)]
+        AA = [[sum(A[i][t] * A[t][j] for t in range(m)) for j in range(m)] for i in range(m)]
+        Bm = [[_bf16_torch(b * A[i][j] + c * AA[i][j]) for j in range(m)] for i in range(m)]
+        X = [[_bf16_torch(h * (a * X[i][j] + sum(Bm[i][t] * X[t][j] for t in range(m)))) for j in range(n)]
+             for i in range(m)]
+    return np.array(X)
+
+
+@pytest.mark.parametrize("m,n,seed", [(2, 3, 20), (3, 5, 21), (3, 3, 22)])
+def test_bf16_contract_matches_scalar_loops(m, n, seed):
+    # Non-diagonal inputs: every rounding point, every term (a X included) and
+    # every index of the contract is checked entry by entry.
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((m, n))
+    xt = O.bf16_round(u)
+    s = 1.0 / (np.linalg.norm(u) + 1e-7)
+    want = _contract_scalar(xt, s)
+    got = O.ns_bf16_contract(xt, s)
+    np.testing.assert_array_equal(got, want)
+    # each step's output lies on the bf16 grid and is not the exact iterate
+    assert np.array_equal(O.bf16_round(got), got)
+    assert O.rel_fro(got, O.ns_exact(xt, s)) > 0
+
+
+def test_bf16_contract_misplaced_rounding_is_detected():
+    # The two placements of the a X term differ on generic input by far more
+    # than one bf16 ulp, so the scalar-loop pin above separates them.
+    rng = np.random.default_rng(23)
+    u = rng.standard_normal((3, 5))
+    xt = O.bf16_round(u)
+    s = 1.0 / (np.linalg.norm(u) + 1e-7)
+    d = np.abs(O.ns_bf16_contract(xt, s) - O.ns_bf16_contract_folded(xt, s))
+    assert d.max() > 0
 
 
 def test_bf16_contract_close_to_exact():
-    # The contract stays within a few percent of exact NS on the body's gradient class.
+    # The contract stays within a few percent of exact NS on the body's gradient
+    # class, and so does the folded placement of a X.
     w = custom_workload(7, [(64, 192, 1, "spike"), (96, 96, 1, "iid")])
     g = gen_grads(w, 0)
     for _gi, _ei, _k, off, r, c in w.submatrices():
         u = g[off:off + r * c].reshape(r, c).astype(np.float64)
         X, _ = O.to_short_side(u)
         s = O.frobenius_scale(u)
-        e = O.rel_fro(O.ns_bf16_contract(O.bf16_round(X), s), O.ns_exact(X, s))
+        ex = O.ns_exact(X, s)
+        e = O.rel_fro(O.ns_bf16_contract(O.bf16_round(X), s), ex)
+        e2 = O.rel_fro(O.ns_bf16_contract_folded(O.bf16_round(X), s), ex)
         assert 1e-3 < e < 4e-2, e
+        assert 1e-3 < e2 < 4e-2, e2
+
+
+def test_rel_fro_hand_values():
+    assert O.rel_fro(np.array([5.0, 12.0]) + np.array([3.0, 4.0]), np.array([5.0, 12.0])) == 5.0 / 13.0
+    assert O.rel_fro(np.zeros((2, 2)), np.zeros((2, 2))) == 0.0
+    assert O.rel_fro(np.ones(3), np.zeros(3)) == math.inf
+    assert O.rel_fro(np.zeros(3), np.array([0.0, 3.0, 4.0])) == 1.0
+    # a Frobenius norm over all entries, not a per-row or spectral norm
+    a = np.array([[1.0, 0.0], [0.0, 0.0]])
+    b = np.array([[0.0, 0.0], [0.0, 2.0]])
+    assert O.rel_fro(a + b, b) == 0.5
+
+
+def test_bf16_ulp_matches_next_bf16_value():
+    # spacing = (next bfloat16 above x) - x, stepping the bit pattern with torch
+    rng = np.random.default_rng(24)
+    x = np.concatenate([np.abs(rng.standard_normal(5000)) * 10.0 ** rng.integers(-30, 30, 5000),
+                        [1.0, 2.0, 3.0, 1e-39, 2.0 ** -126, 2.0 ** -133]]).astype(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    nxt = (xb.view(torch.int16) + 1).view(torch.bfloat16)
+    spacing = (nxt.double() - xb.double()).numpy()
+    np.testing.assert_array_equal(O.bf16_ulp(xb.double().numpy()), spacing)
 
 
 # ---------------------------------------------------------------------------
