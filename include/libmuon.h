@@ -192,7 +192,7 @@ enum {
     MUON_VIEW_STATUS = 6,  /* int32 [num_matrices]: bit 0 = non-finite u seen this step */
     MUON_VIEW_GRAM = 7,    /* the last iteration's A = X X^T: m_pad x m_pad per matrix at its gram_offset
                               (tiled matrices; the one-workgroup path keeps A in LDS, its region is unspecified) */
-    MUON_VIEW_POLY = 8     /* the last iteration's B' = a I + b A + c A A, same layout as MUON_VIEW_GRAM */
+    MUON_VIEW_POLY = 8     /* the last iteration's B = b A + c A A, same layout as MUON_VIEW_GRAM */
 };
 
 /* Device pointer and byte size of an internal buffer, valid after the
@@ -225,8 +225,8 @@ float muon_momentum_warmup(int64_t step, int64_t warmup_steps, float start, floa
 enum {
     MUON_KERNEL_MOMENTUM = 0, /* momentum + Nesterov + cast + sum of squares */
     MUON_KERNEL_GRAM = 1,     /* A = X X^T (upper tiles, mirrored) */
-    MUON_KERNEL_POLY = 2,     /* B = b A + c A^2 */
-    MUON_KERNEL_UPDATE = 3,   /* X <- a X + B X */
+    MUON_KERNEL_POLY = 2,     /* B = b A + c A^2 (upper tiles, mirrored) */
+    MUON_KERNEL_UPDATE = 3,   /* X <- a X + B X (a X added in fp32 before rounding) */
     MUON_KERNEL_NORMUON = 4,  /* NorMuon row factors */
     MUON_KERNEL_APPLY = 5,    /* parameter update */
     MUON_KERNEL_NS_SMALL = 6, /* every Newton-Schulz iteration of the bf16 matrices whose

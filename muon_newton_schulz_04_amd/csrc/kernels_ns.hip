@@ -4,13 +4,14 @@
 // "从源码看 Muon 的分布式正交化实现": the quintic iteration with
 // (a, b, c) = (3.4445, -4.7750, 2.0315) on the normalised, short-side X,
 // run in bf16. It is computed here in the algebraically equal factored form
-//     A = X X^T,   B' = a I + b A + c A A,   X <- B' X   (= a X + (b A + c A^2) X)
+//     A = X X^T,   B = b A + c A A,   X <- a X + B X
 // with three kernels per iteration:
 //   GRAM    A = alpha X X^T            (only tiles ti <= tj; the mirror tile is
 //                                       written from the same registers)
-//   POLY    B' = a I + b A + c A A^T   (A symmetric; the polynomial is the epilogue)
-//   UPDATE  X' = alpha B' X            (X enters as the column-side operand,
-//                                       transposed on its way into LDS)
+//   POLY    B = b A + c A A^T          (A symmetric; the polynomial is the epilogue)
+//   UPDATE  X' = alpha (a X + B X)     (X enters as the column-side operand,
+//                                       transposed on its way into LDS; a X is
+//                                       added in the epilogue, before rounding)
 // bf16 operands with fp32 accumulation (v_mfma_f32_32x32x16_bf16), or fp32
 // throughout (v_mfma_f32_32x32x2_f32) in the fp32 mode. Every output is
 // rounded once to the storage type.
@@ -331,11 +332,11 @@ __global__ __launch_bounds__(kThreads) void k_ns(const MatDesc* __restrict__ mat
                         for (int e = 0; e < 4; ++e) store_scalar<ET>(o + (int64_t)(jb + e) * d.m_pad + i, v[e]);
                     }
                 } else if (MODE == NS_POLY) {
-                    // B' = a I + b A + c A A: the a X term of the update rides on B's diagonal
+                    // B = b A + c A A
                     float av[4];
                     load4<ET>(ain + d.a_off + (int64_t)i * d.m_pad + jb, av);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = fmaf(cb, av[e], cc * v[e]) + (jb + e == i ? ca : 0.0f);
+                    for (int e = 0; e < 4; ++e) v[e] = fmaf(cb, av[e], cc * v[e]);
                     ET* o = out + d.a_off;
                     store4<ET>(o + (int64_t)i * d.m_pad + jb, v[0], v[1], v[2], v[3]);
                     if (w.ti != w.tj) {
@@ -343,8 +344,11 @@ __global__ __launch_bounds__(kThreads) void k_ns(const MatDesc* __restrict__ mat
                         for (int e = 0; e < 4; ++e) store_scalar<ET>(o + (int64_t)(jb + e) * d.m_pad + i, v[e]);
                     }
                 } else {
+                    // X' = alpha (a X + B X)
+                    float xv[4];
+                    load4<ET>(xin + d.x_off + (int64_t)i * d.n_pad + jb, xv);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] *= alpha;
+                    for (int e = 0; e < 4; ++e) v[e] = fmaf(ca, xv[e], v[e]) * alpha;
                     store4<ET>(out + d.x_off + (int64_t)i * d.n_pad + jb, v[0], v[1], v[2], v[3]);
                     if (rowstats) {
 #pragma unroll

@@ -29,10 +29,15 @@
 //  * The fragment reads of sub-step k+1 run under the MFMAs of sub-step k.
 //  * On diagonal Gram / polynomial tiles both operands are the same rows,
 //    which are loaded once.
-//  * The a X term of the update is folded into the polynomial: the poly
-//    kernel writes B' = a I + b A + c A A, so the update is the pure product
-//    X' = alpha B' X and reads X once per iteration. The poly kernel's own
-//    A tile (for the b A term) streams into LDS during its last K slice.
+//  * The update computes X' = alpha (a X + B X) with B = b A + c A A as the
+//    polynomial kernel rounded it. The a X term needs the output tile's own
+//    rows of X, which pass through LDS as the K slices that cover the tile's
+//    row range: while such a slice is resident, each wave adds a times its
+//    entries to the accumulators of the rows it owns (8-byte LDS reads laid
+//    out like the accumulators), so X is still read once per iteration and
+//    a X is summed in fp32 before the single rounding of X'. The polynomial
+//    kernel's own A tile (for the b A term) streams into LDS during its last
+//    K slice.
 //
 // Source of the iteration: [P4] "modded-nanogpt 50B-token 长时程训练实验解析",
 // section "从源码看 Muon 的分布式正交化实现" (quintic Newton–Schulz in bf16).
@@ -80,17 +85,30 @@ __device__ __forceinline__ bf16x4 tr_read(const char* p) {
 // flight (vmcnt(0)) before LDS reads it cannot prove disjoint, which undoes
 // the ring; the kernel orders the ring itself with explicit vmcnt waits and
 // barriers, and every such load has completed before any compiler-managed
-// vector memory wait (the epilogue) is reached. No other code of this kernel
-// uses M0.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int voff, int soff) {
-    const uint32_t m0v = (uint32_t)(uintptr_t)(LDS_AS char*)lds;
+// vector memory wait (the epilogue) is reached. M0 is not named as clobbered:
+// the compiler reserves it and rejects it in a clobber list; it writes M0
+// only for LDS DMA, GDS and message instructions, and this kernel has none
+// besides these loads.
+__device__ __forceinline__ void dma16(u32x4 r, char* lds, int voff, int soff) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)lds);
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "v"(voff), "s"(r), "s"(soff), "s"(m0v));
+                 : "v"(voff), "s"(r), "s"(soff), "s"(m0v)
+                 );
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+// Buffer resource of `bytes` bytes at `base` (stride 0, raw buffer): word 0
+// and the low half of word 1 hold the address, word 2 the byte range that
+// the hardware bounds-checks, word 3 the format word. Built from wave-uniform
+// words (readfirstlane) so that it stays in scalar registers.
+__device__ __forceinline__ u32x4 rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
 }
 
 // The 32 x 32 blocks a wave computes on a diagonal tile (on or above the
@@ -161,7 +179,12 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     // the ring, or the epilogue's staged rows plus a small reduction area at
     // the top (the Gram's first-iteration norm; the ring is idle by then)
     constexpr int REDB = 64;
-    constexpr int SMEM = NBUF * LY::STAGE > T * EROW + REDB ? NBUF * LY::STAGE : T * EROW + REDB;
+    // POLY / UPDATE add a spare region after the ring for part of the output
+    // tile's own block (below); 160 KB is the workgroup's LDS limit
+    constexpr int RING = NBUF * LY::STAGE;
+    constexpr int SPARE_BYTES = MODE == NS_GRAM ? 0 : (160 * 1024 - RING < T * 2 * T ? 160 * 1024 - RING : T * 2 * T);
+    constexpr int SPARE_OFF = RING;
+    constexpr int SMEM = RING + SPARE_BYTES > T * EROW + REDB ? RING + SPARE_BYTES : T * EROW + REDB;
     static_assert(FRJ >= 1 && NWV % 2 == 0 && NWV * 4 <= REDB, "tile too small for this wave grid");
 
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -211,9 +234,10 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         ldq = d.n_pad;
         K = (d.m + BK - 1) / BK * BK;
     }
+    const int nk = K / BK;  // >= 3 for the Gram (K >= 96), >= 2 otherwise (K >= 128): m > 64 here
     // buffer ranges: the tile's rows (P, and Q for Gram / poly) or all K rows of X
-    const __amdgpu_buffer_rsrc_t rp = rsrc(Psrc, (uint32_t)(T * ldp * 2));
-    const __amdgpu_buffer_rsrc_t rq =
+    const u32x4 rp = rsrc(Psrc, (uint32_t)(T * ldp * 2));
+    const u32x4 rq =
         rsrc(Qsrc, (uint32_t)((MODE == NS_UPDATE ? K * ldq : T * ldq) * 2));
 
     // ---- direct-to-LDS load geometry ----
@@ -315,23 +339,36 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             }
         }
     };
-    // POLY: the output tile's own A block (for the b A term) comes into LDS as
-    // 2T-byte rows, ARPB rows per stage buffer, chunk c of row r at c ^ (r & 15);
-    // part q (rows q ARPB ..) goes to buffer (nk + q) % NBUF: parts 0 .. NBUF-2
-    // load during the last K slice (into the buffers it leaves free), the
-    // last part (T = 256) once that slice is done
-    constexpr int ARPB = LY::STAGE / LY::XROWB;
-    constexpr int NAP = T / ARPB;
-    static_assert(MODE != NS_POLY || (T % ARPB == 0 && NAP <= NBUF), "A tile layout");
+    // The output tile's own block of the stage's input, for the epilogue:
+    // POLY needs A[i0.., j0..] for its b A term, UPDATE needs X[i0.., j0..]
+    // for its a X term (X' = alpha (a X + B X), a X added in fp32 before the
+    // single rounding). It comes into LDS as 2T-byte rows, chunk c of row r
+    // at c ^ (r & 15), in three regions so that most of it lands under MFMA
+    // work: rows 0 .. NSP-1 in the spare region beyond the ring, loaded at
+    // the start of the second-to-last K slice; the next ARPB rows in the ring
+    // buffer the last slice leaves free, loaded at its start; the rest (T =
+    // 256: 64 rows) into the last slice's buffer once that slice is done.
+    constexpr bool OWN = MODE != NS_GRAM;
+    constexpr int ARPB = LY::STAGE / LY::XROWB;               // rows of one ring buffer
+    constexpr int NSP = SPARE_BYTES / LY::XROWB < T ? SPARE_BYTES / LY::XROWB : T;  // spare rows
+    constexpr int NRB = T - NSP < ARPB ? T - NSP : ARPB;      // rows in the free ring buffer
+    constexpr int NLAST = T - NSP - NRB;                       // rows loaded after the main loop
+    static_assert(!OWN || (NSP % XROUND == 0 && NRB % XROUND == 0 && NLAST % XROUND == 0 && NLAST <= ARPB),
+                  "own-tile layout");
+    using NSP_C = std::integral_constant<int, NSP>;
+    const int ldo = MODE == NS_UPDATE ? d.n_pad : d.m_pad;
     const int ar = wave * XRPI + lane / XCH;
-    const int va = ar * d.m_pad * 2 + ((lane % XCH) ^ (ar & 15)) * 16;
-    auto dma_apart = [&](int part, char* buf) {
-        if constexpr (MODE == NS_POLY) {
-            const __amdgpu_buffer_rsrc_t ra =
-                rsrc(ain + d.a_off + (int64_t)i0 * d.m_pad + j0, (uint32_t)(T * d.m_pad * 2));
+    const int va = ar * ldo * 2 + ((lane % XCH) ^ (ar & 15)) * 16;
+    // rows row0 .. row0 + N-1 of the own tile -> LDS at dst (N multiple of XROUND)
+    auto dma_own = [&](char* dst, int row0, auto n_c) __attribute__((always_inline)) {
+        if constexpr (OWN) {
+            constexpr int N = decltype(n_c)::value;
+            const bf16* src = MODE == NS_UPDATE ? xin + d.x_off + (int64_t)i0 * d.n_pad + j0
+                                                : ain + d.a_off + (int64_t)i0 * d.m_pad + j0;
+            const u32x4 ra = rsrc(src, (uint32_t)(T * ldo * 2));
 #pragma unroll
-            for (int q = 0; q < ARPB / XROUND; ++q)
-                dma16(ra, buf + (q * XROUND + wave * XRPI) * LY::XROWB, va, (part * ARPB + q * XROUND) * d.m_pad * 2);
+            for (int q = 0; q < N / XROUND; ++q)
+                dma16(ra, dst + (q * XROUND + wave * XRPI) * LY::XROWB, va, (row0 + q * XROUND) * ldo * 2);
         }
     };
 
@@ -359,7 +396,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     // of S; the explicit waits and barriers order the ring.
     constexpr int NKS = BK / 16;  // k16 sub-steps per stage
     auto stage = [&](const char* __restrict__ S, const char* __restrict__ N1, char* __restrict__ NL, int kt,
-                     auto load_c, auto wait_c, auto mask_c) {
+                     auto load_c, auto wait_c, auto mask_c, auto spare_c) __attribute__((always_inline)) {
         constexpr bool LOAD = decltype(load_c)::value;
         constexpr int WAIT = decltype(wait_c)::value;
         constexpr int NF = bit_count(decltype(mask_c)::value);
@@ -367,6 +404,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         using ICH = std::integral_constant<int, NF / 2>;
         using ICN = std::integral_constant<int, NF>;
         if constexpr (LOAD) dma_stage(kt + D, NL);
+        if constexpr (decltype(spare_c)::value) dma_own(smem + SPARE_OFF, 0, NSP_C{});  // own rows 0 .. NSP-1
 #pragma unroll
         for (int ks = 0; ks < NKS - 1; ++ks) {
             const int set = ks & 1;
@@ -396,16 +434,15 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             }
             if (NREAD > NF / 2) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NF / 2, 0);
         } else {
-            if constexpr (MODE == NS_POLY) {
-#pragma unroll
-                for (int q = 0; q < NAP && q < NBUF - 1; ++q) dma_apart(q, smem + ((kt + 1 + q) % NBUF) * LY::STAGE);
+            if constexpr (OWN) {
+                // nk >= 2: the second-to-last slice already sent rows 0 .. NSP-1
+                dma_own(smem + ((kt + 1) % NBUF) * LY::STAGE, NSP, std::integral_constant<int, NRB>{});
             }
             mfma_block(SL, IC0{}, ICN{}, mask_c);
             __syncthreads();
         }
     };
 
-    const int nk = K / BK;  // >= 3 for the Gram (K >= 96), >= 2 otherwise (K >= 128): m > 64 here
     static_assert(D <= 4, "ring depth");
     auto buf = [&](int k) { return smem + (k % NBUF) * LY::STAGE; };
 #pragma unroll
@@ -418,19 +455,31 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     using C2 = std::integral_constant<int, 2>;
     using CD = std::integral_constant<int, D - 1>;
     using CL = std::integral_constant<int, -1>;
-    auto main_loop = [&](auto mask_c) {
-        for (int kt = 0; kt < nk - D; ++kt) stage(buf(kt), buf(kt + 1), buf(kt + D), kt, std::true_type{}, CD{}, mask_c);
-        if constexpr (D >= 4) stage(buf(nk - 4), buf(nk - 3), buf(nk), nk - 4, std::false_type{}, C2{}, mask_c);
-        if constexpr (D >= 3) stage(buf(nk - 3), buf(nk - 2), buf(nk), nk - 3, std::false_type{}, C1{}, mask_c);
-        if constexpr (D >= 2) stage(buf(nk - 2), buf(nk - 1), buf(nk + 1), nk - 2, std::false_type{}, C0{}, mask_c);
-        stage(buf(nk - 1), buf(nk), buf(nk + 2), nk - 1, std::false_type{}, CL{}, mask_c);
+    using NO = std::false_type;
+    auto main_loop = [&](auto mask_c) __attribute__((always_inline)) {
+        if constexpr (OWN) {
+            // D = 1; the second-to-last slice also sends own rows to the spare
+            static_assert(D == 1, "own-tile schedule");
+            for (int kt = 0; kt < nk - 2; ++kt)
+                stage(buf(kt), buf(kt + 1), buf(kt + 1), kt, std::true_type{}, CD{}, mask_c, NO{});
+            stage(buf(nk - 2), buf(nk - 1), buf(nk - 1), nk - 2, std::true_type{}, CD{}, mask_c, std::true_type{});
+            stage(buf(nk - 1), buf(nk), buf(nk + 2), nk - 1, std::false_type{}, CL{}, mask_c, NO{});
+        } else {
+            for (int kt = 0; kt < nk - D; ++kt)
+                stage(buf(kt), buf(kt + 1), buf(kt + D), kt, std::true_type{}, CD{}, mask_c, NO{});
+            if constexpr (D >= 4) stage(buf(nk - 4), buf(nk - 3), buf(nk), nk - 4, std::false_type{}, C2{}, mask_c, NO{});
+            if constexpr (D >= 3) stage(buf(nk - 3), buf(nk - 2), buf(nk), nk - 3, std::false_type{}, C1{}, mask_c, NO{});
+            if constexpr (D >= 2)
+                stage(buf(nk - 2), buf(nk - 1), buf(nk + 1), nk - 2, std::false_type{}, C0{}, mask_c, NO{});
+            stage(buf(nk - 1), buf(nk), buf(nk + 2), nk - 1, std::false_type{}, CL{}, mask_c, NO{});
+        }
     };
     constexpr unsigned FULL = (1u << (FRI * FRJ)) - 1;
     if (MODE == NS_UPDATE || !same) {
         // Edge tiles of padded matrices: output rows >= m and columns >= m
-        // (Gram, polynomial) or >= n (update) are zero (P there is a I, which
-        // the epilogue adds), so a wave skips its 32 x 32 blocks that lie
-        // wholly in the padding. RV: its row blocks below the edge; CM: 2 if
+        // (Gram, polynomial) or >= n (update) are zero (so are A, B and X
+        // there), so a wave skips its 32 x 32 blocks that lie wholly in the
+        // padding. RV: its row blocks below the edge; CM: 2 if
         // both column blocks are inside, 1 if only block wj (the other,
         // 2 WN - 1 - wj, is further right). All waves still run every stage's
         // loads and barriers.
@@ -457,8 +506,8 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             if (wave == W) main_loop(std::integral_constant<unsigned, diag_mask(W / WN, W % WN, WN, FRI)>{});
         });
     }
-    if constexpr (MODE == NS_POLY) {
-        if constexpr (NAP == NBUF) dma_apart(NBUF - 1, buf(nk + NBUF - 1));
+    if constexpr (OWN) {
+        if constexpr (NLAST > 0) dma_own(buf(nk - 1), NSP + NRB, std::integral_constant<int, NLAST>{});
         wait_vm0();
         __syncthreads();
     }
@@ -484,30 +533,66 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     }
     if (MODE == NS_UPDATE && first) alpha = scale_arr[w.mat];
 
-    // Output tiles are staged in LDS as bf16 rows of EROW bytes (2T + 8: 32
-    // consecutive rows start in distinct 8-byte bank slots) and leave as
-    // whole cache lines.
+    // Gram / polynomial output tiles are staged in LDS as bf16 rows of EROW
+    // bytes (2T + 8: 32 consecutive rows start in distinct 8-byte bank slots)
+    // and leave as whole cache lines; the update's tile leaves from its own
+    // X tile's layout.
     auto lds64 = [&](int off) -> uint2& { return *reinterpret_cast<uint2*>(smem + off); };
 
     float rsq[FRI];
 #pragma unroll
     for (int f = 0; f < FRI; ++f) rsq[f] = 0.f;
 
-    uint2 ev[FRI][FRJ][4];
-    // POLY: lane's A entries A[il][jl .. jl+3] (il & 15 == l32 & 15)
-    // (row il lives in part il / ARPB, at buffer (nk + part) % NBUF; ARPB is a
-    // multiple of 32, so a lane's 32-row blocks stay within one part)
-    constexpr int ARPB_E = LY::STAGE / LY::XROWB;
-    auto abase = [&](int il) -> const char* {
-        return smem + ((nk + il / ARPB_E) % NBUF) * LY::STAGE + (il % ARPB_E) * LY::XROWB + 8 * hi;
+    // POLY / UPDATE: the own tile's row r (r & 15 selects its chunk swizzle)
+    // lives in the spare region, the ring buffer the last slice left free, or
+    // the last slice's buffer
+    auto own_row = [&](int r) -> char* {
+        return r < NSP ? smem + SPARE_OFF + r * LY::XROWB
+               : r < NSP + NRB ? smem + (nk % NBUF) * LY::STAGE + (r - NSP) * LY::XROWB
+                               : smem + ((nk - 1) % NBUF) * LY::STAGE + (r - NSP - NRB) * LY::XROWB;
     };
     const int asw = l32 & 15;
+    if constexpr (MODE == NS_UPDATE) {
+        // X' = alpha (a X + B X), in place: each lane reads its own 8-byte
+        // groups X[il][jl .. jl+3] from the own tile and writes the rounded
+        // result back to the same bytes (no other lane touches them); the
+        // tile then leaves from this layout
+#pragma unroll
+        for (int fi = 0; fi < FRI; ++fi) {
+            char* row = own_row(wi * WTM + fi * 32 + l32) + 8 * hi;
+#pragma unroll
+            for (int fj = 0; fj < FRJ; ++fj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint2* pv = reinterpret_cast<uint2*>(row + 16 * ((4 * colblk(fj) + g) ^ asw));
+                    const uint2 xv = *pv;
+                    float v[4];
+                    v[0] = fmaf(ca, bf16_lo(xv.x), acc[fi][fj][4 * g + 0]) * alpha;
+                    v[1] = fmaf(ca, bf16_hi(xv.x), acc[fi][fj][4 * g + 1]) * alpha;
+                    v[2] = fmaf(ca, bf16_lo(xv.y), acc[fi][fj][4 * g + 2]) * alpha;
+                    v[3] = fmaf(ca, bf16_hi(xv.y), acc[fi][fj][4 * g + 3]) * alpha;
+                    uint2 ow;
+                    ow.x = pack_bf16x2(v[0], v[1]);
+                    ow.y = pack_bf16x2(v[2], v[3]);
+                    *pv = ow;
+                    if (ROWSTATS) {
+                        const float r0 = bf16_lo(ow.x), r1 = bf16_hi(ow.x), r2 = bf16_lo(ow.y), r3 = bf16_hi(ow.y);
+                        rsq[fi] = fmaf(r0, r0, rsq[fi]);
+                        rsq[fi] = fmaf(r1, r1, rsq[fi]);
+                        rsq[fi] = fmaf(r2, r2, rsq[fi]);
+                        rsq[fi] = fmaf(r3, r3, rsq[fi]);
+                    }
+                }
+        }
+        __syncthreads();
+    } else {
+    uint2 ev[FRI][FRJ][4];
     // the A entries of one 32-row block (8 loads), read a block ahead of their
     // use so the LDS latency is paid once per block, not once per load
     uint2 a_cur[FRJ][4], a_nxt[FRJ][4];
     auto read_a = [&](int fi, uint2 (&dst)[FRJ][4]) {
-        if constexpr (MODE == NS_POLY) {
-            const char* row = abase(wi * WTM + fi * 32 + l32);
+        if constexpr (OWN) {
+            const char* row = own_row(wi * WTM + fi * 32 + l32) + 8 * hi;
 #pragma unroll
             for (int fj = 0; fj < FRJ; ++fj)
 #pragma unroll
@@ -518,8 +603,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     read_a(0, a_nxt);
 #pragma unroll
     for (int fi = 0; fi < FRI; ++fi) {
-        const int il = wi * WTM + fi * 32 + l32;
-        if constexpr (MODE == NS_POLY) {
+        if constexpr (OWN) {
 #pragma unroll
             for (int fj = 0; fj < FRJ; ++fj)
 #pragma unroll
@@ -531,22 +615,16 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         for (int fj = 0; fj < FRJ; ++fj) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int jl = 32 * colblk(fj) + 8 * g + 4 * hi;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = acc[fi][fj][4 * g + e];
                 if (MODE == NS_POLY) {
-                    // P = a I + b A + c A A: the a X term of the update rides on P's diagonal
+                    // B = b A + c A A
                     const uint2 in = a_cur[fj][g];
                     v[0] = fmaf(cb, bf16_lo(in.x), cc * v[0]);
                     v[1] = fmaf(cb, bf16_hi(in.x), cc * v[1]);
                     v[2] = fmaf(cb, bf16_lo(in.y), cc * v[2]);
                     v[3] = fmaf(cb, bf16_hi(in.y), cc * v[3]);
-                    if (w.ti == w.tj) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (jl + e == il) v[e] += ca;
-                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] *= alpha;
@@ -555,17 +633,10 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
                 ow.x = pack_bf16x2(v[0], v[1]);
                 ow.y = pack_bf16x2(v[2], v[3]);
                 ev[fi][fj][g] = ow;
-                if (MODE == NS_UPDATE && ROWSTATS) {
-                    const float r0 = bf16_lo(ow.x), r1 = bf16_hi(ow.x), r2 = bf16_lo(ow.y), r3 = bf16_hi(ow.y);
-                    rsq[fi] = fmaf(r0, r0, rsq[fi]);
-                    rsq[fi] = fmaf(r1, r1, rsq[fi]);
-                    rsq[fi] = fmaf(r2, r2, rsq[fi]);
-                    rsq[fi] = fmaf(r3, r3, rsq[fi]);
-                }
             }
         }
     }
-    if (MODE == NS_POLY) __syncthreads();  // the A tile is read; LDS is reused below
+    if (OWN) __syncthreads();  // the A tile is read; LDS is reused below
 #pragma unroll
     for (int fi = 0; fi < FRI; ++fi)
 #pragma unroll
@@ -574,6 +645,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             for (int g = 0; g < 4; ++g)
                 lds64((wi * WTM + fi * 32 + l32) * EROW + 2 * (32 * colblk(fj) + 8 * g + 4 * hi)) = ev[fi][fj][g];
     __syncthreads();
+    }
 
     // the tile itself: each thread moves 16-byte row chunks, a wave covers
     // whole rows. The update's output is stored nontemporally: a round of
@@ -590,9 +662,14 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             const int r = id / CPR, c = id % CPR;
             // a diagonal tile's blocks below the diagonal come from the mirror below
             if (MODE != NS_UPDATE && same && (c >> 2) < (r >> 5)) continue;
-            const uint2 lo = lds64(r * EROW + 16 * c);
-            const uint2 up = lds64(r * EROW + 16 * c + 8);
-            const u32x4 wv = {lo.x, lo.y, up.x, up.y};
+            u32x4 wv;
+            if constexpr (MODE == NS_UPDATE) {
+                wv = *reinterpret_cast<const u32x4*>(own_row(r) + 16 * (c ^ (r & 15)));
+            } else {
+                const uint2 lo = lds64(r * EROW + 16 * c);
+                const uint2 up = lds64(r * EROW + 16 * c + 8);
+                wv = u32x4{lo.x, lo.y, up.x, up.y};
+            }
             if (MODE == NS_UPDATE)
                 __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(obase + (int64_t)r * ld + 8 * c));
             else

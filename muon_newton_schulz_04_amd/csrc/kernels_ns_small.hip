@@ -4,21 +4,22 @@
 // side n_pad is at most 512 are too small for the tiled GEMM launches: one
 // 64 x 64 output tile per GEMM and 15 launches a step leave the chip idle.
 // Here one workgroup of 4 waves takes one such matrix through every
-// iteration with X, A and P resident in LDS:
+// iteration with X, A and B resident in LDS:
 //   load X~ (bf16, canonical, padded) -> LDS
 //   per iteration k:  A = R(alpha X X^T)            alpha = s^2 (k = 0) or 1
-//                     P = R(a_k I + b_k A + c_k A A)
-//                     X = R(beta P X)                beta = s (k = 0) or 1
+//                     B = R(b_k A + c_k A A)
+//                     X = R(beta (a_k X + B X))      beta = s (k = 0) or 1
 //   store X (the Newton–Schulz output) and, for NorMuon, the row sums of X^2
 // with R the bf16 rounding and fp32 accumulation, i.e. exactly the rounding
 // points of the tiled path, and s = 1 / (||u||_F + eps) from the momentum
 // kernel's per-tile partial sums.
 //
 // GEMMs are v_mfma_f32_32x32x16_bf16 over 32 x 32 blocks: the 64 x 64
-// symmetric A and P are computed as three blocks (waves 0, 1, 3) with the
-// off-diagonal block mirrored, and X' = P X as 32 x 32 blocks of all four
-// waves. Lane (l32, hi) of a block holds C[l32][8 g + 4 hi + e] in
-// acc[4 g + e], as in the tiled kernels.
+// symmetric A and B are computed as three blocks (waves 0, 1, 3) with the
+// off-diagonal block mirrored, and X' = a X + B X as 32 x 32 blocks of all
+// four waves (a X read from the resident X, added in fp32 before rounding).
+// Lane (l32, hi) of a block holds C[l32][8 g + 4 hi + e] in acc[4 g + e], as
+// in the tiled kernels.
 //
 // Source of the iteration: [P4] "modded-nanogpt 50B-token 长时程训练实验解析",
 // section "从源码看 Muon 的分布式正交化实现" (quintic Newton–Schulz in bf16).
@@ -34,7 +35,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int SM = 64;              // m_pad of a small matrix
-constexpr int AROW = 2 * SM + 16;   // bytes per padded row of A / P
+constexpr int AROW = 2 * SM + 16;   // bytes per padded row of A / B
 
 __device__ __forceinline__ bf16x4 tr_read(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(LDS_AS char*)p);
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(const MatDesc* __restrict
     const int XR = 2 * np + 16;  // bytes per padded row of X
     char* Xb[2] = {sm, sm + SM * XR};
     char* A = sm + 2 * SM * XR;
-    char* P = A + SM * AROW;
+    char* P = A + SM * AROW;  // B = b A + c A A
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(const MatDesc* __restrict
     const int wj = wave & 1;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
-    const bool sym = !(wi == 1 && wj == 0);  // blocks (0,0), (0,1), (1,1) of A and P
+    const bool sym = !(wi == 1 && wj == 0);  // blocks (0,0), (0,1), (1,1) of A and B
 
     // X~ -> LDS (16-byte chunks, rows padded)
     const int cpr = np / 8;
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(const MatDesc* __restrict
             put_block(A, AROW, v, i, wj * 32, wi != wj);
         }
         __syncthreads();
-        // ---- P = a I + b A + c A A (A symmetric: (A A)_ij = sum_k A_ik A_jk) ----
+        // ---- B = b A + c A A (A symmetric: (A A)_ij = sum_k A_ik A_jk) ----
         if (sym) {
             f32x16 acc;
 #pragma unroll
@@ -150,16 +151,12 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(const MatDesc* __restrict
                 const uint2 a2 = *reinterpret_cast<const uint2*>(A + i * AROW + 2 * j);
                 const float av[4] = {bf16_lo(a2.x), bf16_hi(a2.x), bf16_lo(a2.y), bf16_hi(a2.y)};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float x = fmaf(cb, av[e], cc * acc[4 * g + e]);
-                    if (j + e == i) x += ca;
-                    v[4 * g + e] = x;
-                }
+                for (int e = 0; e < 4; ++e) v[4 * g + e] = fmaf(cb, av[e], cc * acc[4 * g + e]);
             }
             put_block(P, AROW, v, i, wj * 32, wi != wj);
         }
         __syncthreads();
-        // ---- X' = beta P X, 64-column chunks, wave (wi, wj): rows wi, cols wj of a chunk ----
+        // ---- X' = beta (a X + B X), 64-column chunks, wave (wi, wj): rows wi, cols wj of a chunk ----
         {
             const float beta = k == 0 ? s : 1.0f;
             const int g16 = lane >> 4, s16 = lane & 15;
@@ -180,7 +177,12 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(const MatDesc* __restrict
                 }
                 float v[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) v[r] = acc[r] * beta;
+                for (int g = 0; g < 4; ++g) {
+                    const uint2 x2 = *reinterpret_cast<const uint2*>(X + i * XR + 2 * (cb0 + 8 * g + 4 * hi));
+                    const float xv[4] = {bf16_lo(x2.x), bf16_hi(x2.x), bf16_lo(x2.y), bf16_hi(x2.y)};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[4 * g + e] = fmaf(ca, xv[e], acc[4 * g + e]) * beta;
+                }
                 put_block(Xn, XR, v, i, cb0, false);
             }
         }

@@ -62,8 +62,8 @@ hipError_t launch_reset(const LaunchCtx& L, float* mom);
 // One Newton–Schulz iteration stage over a work list.
 //   GRAM:   out = alpha * X X^T (upper tiles, mirrored); iteration 0: alpha = s^2
 //           from the momentum partials (and s, sum u^2, status are recorded)
-//   POLY:   out = a I + b A + c A A^T (upper tiles, mirrored)
-//   UPDATE: out = alpha B' X; iteration 0: alpha = s, else 1;
+//   POLY:   out = b A + c A A^T (upper tiles, mirrored)
+//   UPDATE: out = alpha (a X + B X); iteration 0: alpha = s, else 1;
 //           rowstats: per-row partial sums of out^2 for NorMuon
 hipError_t launch_ns_stage(const LaunchCtx& L, const GemmList& G, int mode, const void* xin, const void* ain,
                            void* out, float ca, float cb, float cc, int first, float eps, int rowstats);

@@ -4,11 +4,23 @@ Drives libmuon through its C ABI (binding.MuonHandle) on seeded synthetic
 inputs and compares every stage with the CPU oracle, per matrix:
   G1 momentum           (free-running)              rel. Frobenius <= 1e-6
   G2 X~ = bf16(u)        (u from the GPU's momentum)  within 1 bf16 ulp + fp32 blend error
-  G3 Newton-Schulz      (given the GPU's X~ and s)  <= 2e-2 bf16 contract / 1e-4 fp32 vs exact;
-     beyond 5 iterations, bf16: <= max(2e-2, the contract's own distance from exact NS);
-     for rank-deficient inputs (contract >5e-2 from exact NS) the 2e-2 gate
-     applies to the dominant singular subspace, and the GPU must be no further
-     from exact NS than 1.25x the contract's own distance + 2e-2
+  G3 Newton-Schulz      (given the GPU's X~ and s)
+     fp32 mode: <= 1e-4 vs exact NS;
+     bf16 mode:
+       (a) <= 2e-2 vs the bf16 rounding contract (oracle.ns_bf16_contract):
+           at the workloads' five iterations, or with a coefficient table
+           whose tail converges (the sharp cases); for rank-deficient input
+           (the contract itself > 5e-2 from exact NS) on the span of the
+           singular directions with normalised sigma >= 1e-2, because outside
+           it the output is rounding noise amplified up to a^5 ~ 485x and two
+           correct bf16 roundings differ there (the full-matrix figure is
+           reported, not gated);
+       (b) ||GPU - exact|| <= ||contract - exact|| + slack on every bf16 case:
+           the GPU is no worse an approximation of exact NS than the contract.
+           slack = 5e-3 up to ten iterations (the pages' range of 5-10);
+           beyond it the non-converging quintic keeps injecting rounding noise
+           and two correct implementations drift apart by up to the method's
+           own error, so the bound is 1.5 ||contract - exact|| + 5e-3.
   G4 NorMuon v, params  (given the GPU's O, v, p)   <= 1e-6
 """
 
@@ -24,17 +36,21 @@ from workloads import gen_grads, gen_matrix_grad, gen_params
 TOL_MOM = 1e-6
 TOL_NS_BF16 = 2e-2
 TOL_NS_FP32 = 1e-4
-# The 2e-2 bf16 gate is stated for the five Newton-Schulz iterations of every
-# workload. The quintic does not converge (its singular values keep moving in
-# [0.68, 1.20]), so with more iterations two bf16 implementations with the
-# same rounding points but different accumulation orders drift further apart
-# each step; beyond five the GPU result must be no farther from the contract
-# than the contract is from exact NS (and the gate is never tighter than 2e-2).
-NS_STEPS_SPEC = 5
+TOL_NS_EXACT_SLACK = 5e-3  # G3(b): allowed excess over the contract's own distance from exact NS
+NS_STEPS_SPEC = 5          # the iteration count G3(a) is stated for
+NS_STEPS_PAGES_MAX = 10    # the pages' range of iteration counts is 5-10
+ILL_CONDITIONED = 5e-2     # contract vs exact NS above this: the input is rank-deficient
+SIGNAL_SIGMA = 1e-2        # normalised singular values above this span the dominant subspace
 TOL_PARAM = 1e-6
 TOL_DELTA = 1e-4  # the update p_new - p_old itself (float32 rounding of p bounds it)
-ILL_CONDITIONED = 5e-2  # bf16-contract vs exact NS above this: the input is rank-deficient
-SIGNAL_SIGMA = 1e-2     # normalised singular values above this span the dominant subspace
+
+
+def exact_bound(ce: float, iterations: int) -> float:
+    """G3(b): the largest allowed ||GPU - exact|| / ||exact|| for a bf16 result
+    whose contract lies ce from exact NS after `iterations` iterations."""
+    if iterations <= NS_STEPS_PAGES_MAX:
+        return ce + TOL_NS_EXACT_SLACK
+    return 1.5 * ce + TOL_NS_EXACT_SLACK
 
 
 def hp_for(w, **over):
@@ -104,11 +120,14 @@ class GpuRun:
 
 
 def check_stages(run: GpuRun, step: int, indices, grads_host=None, p_prev=None, v_prev=None,
-                 orc_m=None, report=None):
+                 orc_m=None, report=None, coeffs=None, sharp=None):
     """Staged gates for the matrices in `indices` after `run.step()` at `step`.
 
     orc_m: dict gi -> oracle float64 momentum before this step (updated in place).
     p_prev / v_prev: dict gi -> GPU params / NorMuon v before this step.
+    coeffs: the run's coefficient table (default: the pages' quintic at the
+    run's iteration count); sharp: whether G3(a) applies (default: five or
+    fewer iterations).
     """
     w = run.w
     beta = w.momentum
@@ -153,37 +172,37 @@ def check_stages(run: GpuRun, step: int, indices, grads_host=None, p_prev=None, 
         s_or = O.frobenius_scale(u)
         assert abs(s - s_or) <= 1e-5 * s_or + 1e-30, (gi, s, s_or)
         out = run.ns_out(gi)
-        co = O.default_coeffs(run.hp.ns_steps)  # the pages' coefficients, the run's step count
+        co = coeffs if coeffs is not None else O.default_coeffs(run.hp.ns_steps)
+        ex = O.ns_exact(xt, s, co)
         if run.fp32:
-            ref_ns = O.ns_exact(xt, s, co)
-        else:
-            ref_ns = O.ns_bf16_contract(xt, s, co)
-        e3 = O.rel_fro(out, ref_ns)
-        ce = 0.0
-        if not run.fp32:
-            # how far the bf16 method itself is from exact NS on this input
-            ex = O.ns_exact(xt, s, co)
-            ce = O.rel_fro(ref_ns, ex)
-        if ce > ILL_CONDITIONED:
-            # Rank-deficient input: outside the dominant singular subspace the
-            # output is amplified rounding noise (up to a^5 ~ 485x), so two
-            # legitimate bf16 roundings differ there. Gate the dominant
-            # subspace at the bf16 tolerance, and require the GPU to be no
-            # worse an approximation of exact NS than the contract is.
-            U, S, _Vt = np.linalg.svd(xt, full_matrices=False)
-            Us = U[:, S * s >= SIGNAL_SIGMA]
-            e_sig = O.rel_fro(Us.T @ out, Us.T @ ref_ns) if Us.shape[1] else 0.0
-            excess = O.rel_fro(out, ex) - (1.25 * ce + TOL_NS_BF16)
-            worst["ns_ill_signal"] = max(worst.get("ns_ill_signal", 0.0), e_sig)
-            worst["ns_ill_excess"] = max(worst.get("ns_ill_excess", -1.0), excess)
-        elif not run.fp32 and run.hp.ns_steps > NS_STEPS_SPEC:
-            worst["ns_long_excess"] = max(worst.get("ns_long_excess", -1.0), e3 - max(TOL_NS_BF16, ce))
-        else:
+            e3 = O.rel_fro(out, ex)
+            ce = e_ex = 0.0
             if e3 > worst["ns"]:
                 worst["ns_at"] = (gi, R, C, e.gclass)
             worst["ns"] = max(worst["ns"], e3)
+        else:
+            ref_ns = O.ns_bf16_contract(xt, s, co)
+            e3 = O.rel_fro(out, ref_ns)        # GPU vs the contract
+            ce = O.rel_fro(ref_ns, ex)         # the contract vs exact NS (the method's own error)
+            e_ex = O.rel_fro(out, ex)          # GPU vs exact NS
+            worst["ns_exact_excess"] = max(worst.get("ns_exact_excess", -1.0), e_ex - exact_bound(ce, len(co)))
+            sharp_case = sharp if sharp is not None else len(co) <= NS_STEPS_SPEC
+            if not sharp_case:
+                worst["ns_long"] = max(worst.get("ns_long", 0.0), e3)
+            elif ce > ILL_CONDITIONED:
+                U, S, _Vt = np.linalg.svd(xt, full_matrices=False)
+                Us = U[:, S * s >= SIGNAL_SIGMA]
+                e_sig = O.rel_fro(Us.T @ out, Us.T @ ref_ns) if Us.shape[1] else 0.0
+                if e_sig > worst["ns"]:
+                    worst["ns_at"] = (gi, R, C, e.gclass, "signal subspace")
+                worst["ns"] = max(worst["ns"], e_sig)
+                worst["ns_ill_full"] = max(worst.get("ns_ill_full", 0.0), e3)
+            else:
+                if e3 > worst["ns"]:
+                    worst["ns_at"] = (gi, R, C, e.gclass)
+                worst["ns"] = max(worst["ns"], e3)
         if report is not None:
-            report.append(("ns", step, gi, R, C, e.gclass, e3, ce))
+            report.append(("ns", step, gi, R, C, e.gclass, e3, ce, e_ex))
         # G4 NorMuon + params, teacher-forced on the GPU's O
         Oh = out
         if w.normuon:
@@ -203,9 +222,7 @@ def assert_worst(worst, fp32=False):
     if not fp32:
         assert worst["xt_ulp_viol"] == 0, worst
     assert worst["ns"] <= (TOL_NS_FP32 if fp32 else TOL_NS_BF16), worst
-    assert worst.get("ns_ill_signal", 0.0) <= TOL_NS_BF16, worst
-    assert worst.get("ns_ill_excess", -1.0) <= 0.0, worst
-    assert worst.get("ns_long_excess", -1.0) <= 0.0, worst
+    assert worst.get("ns_exact_excess", -1.0) <= 0.0, worst
     assert worst["v"] <= TOL_MOM, worst
     assert worst["param"] <= TOL_PARAM, worst
     assert worst["delta"] <= TOL_DELTA, worst
