@@ -24,9 +24,12 @@
  *    workspace and zeroes its state there, blocking; muon_step and
  *    muon_reset only enqueue work on `stream` and never synchronise.
  *  - Errors: every call returns a muon_status; nothing aborts or throws
- *    across the ABI. Validation happens before any HIP call. A kernel fault
+ *    across the ABI (a host allocation failure inside the library returns
+ *    MUON_E_HOST). Validation happens before any HIP call. A kernel fault
  *    surfaces at the caller's next synchronisation. Handles are not
- *    thread-safe; use one stream per handle per call.
+ *    thread-safe; use one stream per handle per call. muon_step allocates
+ *    no memory, host or device (unless muon_profile_enable turned on its
+ *    event records).
  */
 #ifndef LIBMUON_H
 #define LIBMUON_H
@@ -46,7 +49,8 @@ typedef enum muon_status {
     MUON_E_NO_DEVICE = -4,   /* no HIP device, or the device is not gfx950 */
     MUON_E_HIP = -5,         /* a HIP runtime call failed (see muon_last_error) */
     MUON_E_STATE = -6,       /* misuse of a handle (wrong device current, ...) */
-    MUON_E_WORKSPACE = -7    /* workspace null, misaligned (256 B) or too small */
+    MUON_E_WORKSPACE = -7,   /* workspace null, misaligned (256 B) or too small */
+    MUON_E_HOST = -8         /* host-side failure: out of host memory (the message says what failed) */
 } muon_status;
 
 /* One table entry: `count` contiguous row-major [rows, cols] float32 matrices
@@ -112,7 +116,9 @@ typedef struct muon_handle muon_handle;
 void muon_hparams_default(muon_hparams* hp);
 
 /* Bytes of device workspace muon_init needs for this table and hp.
- * Host-only; validates the table (same errors as muon_init). */
+ * Host-only; validates the table (same errors as muon_init).
+ * Library plumbing: the pages have no counterpart (their optimizer keeps its
+ * buffers in PyTorch tensors). */
 muon_status muon_workspace_bytes(const muon_matrix* table, int32_t n, const muon_hparams* hp,
                                  size_t* out_bytes);
 
@@ -148,17 +154,22 @@ muon_status muon_step(muon_handle* h, float* params, const float* grads, float* 
  * `stream` ([P2] change 2: reset() after warm-up / capture dirtied them). */
 muon_status muon_reset(muon_handle* h, float* momentum, int64_t numel, void* stream);
 
-/* Free the handle (host memory only). NULL is a no-op. */
+/* Free the handle (host memory only). NULL is a no-op. Library plumbing,
+ * not defined by the pages. */
 void muon_destroy(muon_handle* h);
 
-/* Static description of a status code. */
+/* Static description of a status code. Library plumbing, not defined by the
+ * pages. */
 const char* muon_status_string(muon_status s);
 
 /* Detail of the handle's last error ("" if none); NULL handle -> the last
- * error of a failed muon_init / muon_workspace_bytes on this thread. */
+ * error of a failed muon_init / muon_workspace_bytes on this thread. Library
+ * plumbing, not defined by the pages. */
 const char* muon_last_error(const muon_handle* h);
 
-/* ---- introspection (tests and tools) ------------------------------------ */
+/* ---- introspection (tests and tools) ------------------------------------
+ * Library plumbing, not defined by the pages: these expose the library's own
+ * buffers and plan so that tests can compare each stage with an oracle. */
 
 /* Where matrix `index` (0-based over the table with counts expanded) lives
  * in the workspace: short-side shape m <= n, row stride ld (elements) of the
@@ -220,7 +231,8 @@ float muon_lr_cooldown_floor(int64_t step, int64_t main_iterations, float cooldo
  * momentum = (1 - frac) start + frac end ([P3]: 500 steps, 0.85 -> 0.95). */
 float muon_momentum_warmup(int64_t step, int64_t warmup_steps, float start, float end);
 
-/* ---- measurement (benchmarks) ------------------------------------------- */
+/* ---- measurement (benchmarks) -------------------------------------------
+ * Library plumbing, not defined by the pages. */
 
 enum {
     MUON_KERNEL_MOMENTUM = 0, /* momentum + Nesterov + cast + sum of squares */

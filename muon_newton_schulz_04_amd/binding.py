@@ -23,6 +23,7 @@ MUON_E_NO_DEVICE = -4
 MUON_E_HIP = -5
 MUON_E_STATE = -6
 MUON_E_WORKSPACE = -7
+MUON_E_HOST = -8
 
 MUON_MAX_NS_STEPS = 16
 MUON_NS_BF16 = 0

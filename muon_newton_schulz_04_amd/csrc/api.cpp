@@ -12,6 +12,9 @@
 
 #include <cmath>
 #include <cstring>
+#include <exception>
+#include <memory>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -56,12 +59,44 @@ namespace {
 
 thread_local std::string g_last_error;
 
-muon_status fail(muon_handle* h, muon_status s, const std::string& msg) {
-    if (h)
-        h->last_error = msg;
-    else
-        g_last_error = msg;
+// Records msg as the handle's (or this thread's) last error. Never throws:
+// if the message cannot be stored, the status still reaches the caller.
+muon_status fail(muon_handle* h, muon_status s, const std::string& msg) noexcept {
+    try {
+        if (h)
+            h->last_error = msg;
+        else
+            g_last_error = msg;
+    } catch (...) {
+    }
     return s;
+}
+
+muon_status fail(muon_handle* h, muon_status s, const char* msg) noexcept {
+    try {
+        if (h)
+            h->last_error = msg;
+        else
+            g_last_error = msg;
+    } catch (...) {
+    }
+    return s;
+}
+
+// Runs the body of an extern "C" entry point; no exception crosses the ABI:
+// a host allocation failure (or any other exception from the standard
+// library) becomes MUON_E_HOST with its description as the last error.
+template <typename F>
+muon_status guarded(muon_handle* h, const char* where, F&& body) noexcept {
+    try {
+        return body();
+    } catch (const std::bad_alloc&) {
+        return fail(h, MUON_E_HOST, std::string(where) + ": out of host memory");
+    } catch (const std::exception& ex) {
+        return fail(h, MUON_E_HOST, std::string(where) + ": " + ex.what());
+    } catch (...) {
+        return fail(h, MUON_E_HOST, where);
+    }
 }
 
 muon_status hip_fail(muon_handle* h, hipError_t e, const char* where) {
@@ -145,38 +180,35 @@ bool overlap(const void* a, const void* b, int64_t bytes) {
 extern "C" {
 
 muon_status muon_workspace_bytes(const muon_matrix* table, int32_t n, const muon_hparams* hp, size_t* out_bytes) {
-    if (!out_bytes) return fail(nullptr, MUON_E_INVALID_ARG, "null out_bytes");
-    muon::Plan P;
-    std::string err;
-    muon_status s = muon::build_plan(table, n, hp, &P, &err);
-    if (s != MUON_OK) return fail(nullptr, s, err);
-    *out_bytes = P.total_bytes;
-    return MUON_OK;
+    return guarded(nullptr, "muon_workspace_bytes", [&]() -> muon_status {
+        if (!out_bytes) return fail(nullptr, MUON_E_INVALID_ARG, "null out_bytes");
+        muon::Plan P;
+        std::string err;
+        muon_status s = muon::build_plan(table, n, hp, &P, &err);
+        if (s != MUON_OK) return fail(nullptr, s, err);
+        *out_bytes = P.total_bytes;
+        return MUON_OK;
+    });
 }
 
-muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp, void* workspace,
-                      size_t ws_bytes, int32_t device) {
+static muon_status init_impl(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp,
+                             void* workspace, size_t ws_bytes, int32_t device) {
     if (!out) return fail(nullptr, MUON_E_INVALID_ARG, "null handle output");
     *out = nullptr;
-    muon_handle* h = new muon_handle();
+    std::unique_ptr<muon_handle> owner(new muon_handle());
+    muon_handle* h = owner.get();
     std::string err;
     muon_status s = muon::build_plan(table, n, hp, &h->plan, &err);
-    if (s != MUON_OK) {
-        delete h;
-        return fail(nullptr, s, err);
-    }
+    if (s != MUON_OK) return fail(nullptr, s, err);
     const muon::Plan& P = h->plan;
     if (P.total_bytes > 0) {
         if (!workspace) {
-            delete h;
             return fail(nullptr, MUON_E_WORKSPACE, "null workspace");
         }
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) {
-            delete h;
             return fail(nullptr, MUON_E_WORKSPACE, "workspace not 256-byte aligned");
         }
         if (ws_bytes < P.total_bytes) {
-            delete h;
             return fail(nullptr, MUON_E_WORKSPACE,
                         "workspace too small: need " + std::to_string(P.total_bytes) + " bytes");
         }
@@ -184,28 +216,23 @@ muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, co
     int count = 0;
     hipError_t e = hipGetDeviceCount(&count);
     if (e != hipSuccess || count < 1) {
-        delete h;
         return fail(nullptr, MUON_E_NO_DEVICE, "no HIP device");
     }
     if (device < 0 || device >= count) {
-        delete h;
         return fail(nullptr, MUON_E_NO_DEVICE, "device index out of range");
     }
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, device);
     if (e != hipSuccess) {
-        delete h;
         return hip_fail(nullptr, e, "hipGetDeviceProperties");
     }
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
-        delete h;
         return fail(nullptr, MUON_E_NO_DEVICE, std::string("device is ") + prop.gcnArchName + ", need gfx950");
     }
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) prev = -1;
     e = hipSetDevice(device);
     if (e != hipSuccess) {
-        delete h;
         return hip_fail(nullptr, e, "hipSetDevice");
     }
     h->device = device;
@@ -224,6 +251,8 @@ muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, co
         if (e == hipSuccess) e = up(L.off_poly, L.poly.data(), L.poly.size() * sizeof(muon::TileWork));
         if (e == hipSuccess) e = up(L.off_update, L.update.data(), L.update.size() * sizeof(muon::TileWork));
     }
+    // the one-workgroup kernel's dynamic LDS, once for this device
+    if (e == hipSuccess && !P.small.empty()) e = muon::prepare_ns_small(P.small_np);
     for (int g = 0; g + 1 < P.n_groups && e == hipSuccess; ++g) {
         e = hipStreamCreateWithFlags(&h->aux[g], hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork[g], hipEventDisableTiming);
@@ -237,15 +266,20 @@ muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, co
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (prev >= 0) (void)hipSetDevice(prev);
     if (e != hipSuccess) {
-        delete h;
         return hip_fail(nullptr, e, "uploading descriptors");
     }
-    *out = h;
+    *out = owner.release();
     return MUON_OK;
 }
 
-muon_status muon_step(muon_handle* h, float* params, const float* grads, float* momentum, int64_t numel, float lr,
-                      float momentum_coef, void* stream) {
+muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp, void* workspace,
+                      size_t ws_bytes, int32_t device) {
+    return guarded(nullptr, "muon_init",
+                   [&]() { return init_impl(out, table, n, hp, workspace, ws_bytes, device); });
+}
+
+static muon_status step_impl(muon_handle* h, float* params, const float* grads, float* momentum, int64_t numel,
+                             float lr, float momentum_coef, void* stream) {
     if (!h) return fail(nullptr, MUON_E_INVALID_ARG, "null handle");
     const muon::Plan& P = h->plan;
     if (P.active.empty()) return MUON_OK;
@@ -301,9 +335,10 @@ muon_status muon_step(muon_handle* h, float* params, const float* grads, float* 
     // groups' first GEMMs and the parameter updates under the last groups'
     // GEMMs. Launches are issued iteration by iteration, round-robin over the
     // groups, so every stream has work queued early.
-    std::vector<muon::LaunchCtx> Lg(P.n_groups, L);
-    std::vector<hipStream_t> sg(P.n_groups, st);
+    muon::LaunchCtx Lg[muon::kMaxGroups];
+    hipStream_t sg[muon::kMaxGroups];
     for (int grp = 0; grp < P.n_groups; ++grp) {
+        Lg[grp] = L;
         sg[grp] = grp == 0 ? st : h->aux[grp - 1];
         Lg[grp].stream = sg[grp];
         Lg[grp].ew_tile0 = P.ew_begin[grp];
@@ -382,6 +417,12 @@ muon_status muon_step(muon_handle* h, float* params, const float* grads, float* 
     return MUON_OK;
 }
 
+muon_status muon_step(muon_handle* h, float* params, const float* grads, float* momentum, int64_t numel, float lr,
+                      float momentum_coef, void* stream) {
+    return guarded(h, "muon_step",
+                   [&]() { return step_impl(h, params, grads, momentum, numel, lr, momentum_coef, stream); });
+}
+
 muon_status muon_reset(muon_handle* h, float* momentum, int64_t numel, void* stream) {
     if (!h) return fail(nullptr, MUON_E_INVALID_ARG, "null handle");
     const muon::Plan& P = h->plan;
@@ -409,6 +450,7 @@ const char* muon_status_string(muon_status s) {
         case MUON_E_HIP: return "HIP runtime error";
         case MUON_E_STATE: return "invalid handle state";
         case MUON_E_WORKSPACE: return "invalid workspace";
+        case MUON_E_HOST: return "host-side failure";
     }
     return "unknown status";
 }
@@ -503,7 +545,8 @@ muon_status muon_profile_enable(muon_handle* h, int32_t on) {
     return MUON_OK;
 }
 
-muon_status muon_profile_read(muon_handle* h, int32_t kernel, int32_t clear, int64_t* launches, double* total_ms) {
+static muon_status profile_read_impl(muon_handle* h, int32_t kernel, int32_t clear, int64_t* launches,
+                                     double* total_ms) {
     if (!h || !launches || !total_ms) return MUON_E_INVALID_ARG;
     if (kernel < 0 || kernel >= MUON_KERNEL_COUNT) return MUON_E_INVALID_ARG;
     int64_t n = 0;
@@ -528,6 +571,10 @@ muon_status muon_profile_read(muon_handle* h, int32_t kernel, int32_t clear, int
         h->recs.clear();
     }
     return MUON_OK;
+}
+
+muon_status muon_profile_read(muon_handle* h, int32_t kernel, int32_t clear, int64_t* launches, double* total_ms) {
+    return guarded(h, "muon_profile_read", [&]() { return profile_read_impl(h, kernel, clear, launches, total_ms); });
 }
 
 }  // extern "C"

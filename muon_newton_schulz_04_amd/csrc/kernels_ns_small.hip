@@ -216,14 +216,18 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(const MatDesc* __restrict
 
 size_t ns_small_lds_bytes(int n_pad_max) { return (size_t)2 * SM * (2 * n_pad_max + 16) + (size_t)2 * SM * AROW; }
 
+hipError_t prepare_ns_small(int n_pad_max) {
+    if (n_pad_max <= 0) return hipSuccess;
+    return hipFuncSetAttribute((const void*)k_ns_small, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)ns_small_lds_bytes(n_pad_max));
+}
+
 hipError_t launch_ns_small(const LaunchCtx& L, const int32_t* list, int n, int n_pad_max, const NsCoeffs& co,
                            void* out, int rowstats) {
     if (n == 0) return hipSuccess;
-    const size_t lds = ns_small_lds_bytes(n_pad_max);
-    hipError_t e = hipFuncSetAttribute((const void*)k_ns_small, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    k_ns_small<<<n, kThreads, lds, L.stream>>>(L.mats, list, (const bf16*)L.xt, (bf16*)out, co, L.partials, L.ss,
-                                               L.scale, L.status, L.rowpart, rowstats);
+    k_ns_small<<<n, kThreads, ns_small_lds_bytes(n_pad_max), L.stream>>>(L.mats, list, (const bf16*)L.xt, (bf16*)out,
+                                                                         co, L.partials, L.ss, L.scale, L.status,
+                                                                         L.rowpart, rowstats);
     return hipGetLastError();
 }
 

@@ -79,5 +79,8 @@ hipError_t launch_ns_stage_big(const LaunchCtx& L, const GemmList& G, int mode, 
 hipError_t launch_ns_small(const LaunchCtx& L, const int32_t* list, int n, int n_pad_max, const NsCoeffs& co,
                            void* out, int rowstats);
 size_t ns_small_lds_bytes(int n_pad_max);
+// Allow the one-workgroup kernel its dynamic LDS for n_pad up to n_pad_max on
+// the current device (once, at init; launches do not repeat it).
+hipError_t prepare_ns_small(int n_pad_max);
 
 }  // namespace muon

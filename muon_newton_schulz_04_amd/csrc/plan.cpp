@@ -157,6 +157,12 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
             *err = "entry " + std::to_string(e) + ": non-finite lr_mul / wd_mul";
             return MUON_E_INVALID_ARG;
         }
+        // rows, cols <= 2^20 and count <= 2^24: bound rows x cols first, so the
+        // extent below stays far from int64 overflow
+        if (t.rows * t.cols >= (INT64_C(1) << 30)) {
+            *err = "entry " + std::to_string(e) + ": matrix too large for one tile grid";
+            return MUON_E_SHAPE;
+        }
         const int64_t sz = t.rows * t.cols * t.count;
         if (t.offset > (INT64_C(1) << 62) - sz) {
             *err = "entry " + std::to_string(e) + ": extent overflows";

@@ -18,8 +18,10 @@ constexpr float kNaN = std::numeric_limits<float>::quiet_NaN();
 }
 
 extern "C" float muon_lr_wsd(int64_t it, int64_t num_iterations, int64_t warmup_iters, int64_t warmdown_iters) {
+    // warmup_iters > num_iterations - warmdown_iters is the sum check without
+    // an int64 overflow (all three are non-negative here)
     if (it < 0 || num_iterations <= 0 || it >= num_iterations || warmup_iters < 0 || warmdown_iters < 0 ||
-        warmup_iters + warmdown_iters > num_iterations)
+        warmdown_iters > num_iterations || warmup_iters > num_iterations - warmdown_iters)
         return kNaN;
     if (it < warmup_iters) return (float)((double)(it + 1) / (double)warmup_iters);
     if (it < num_iterations - warmdown_iters) return 1.0f;

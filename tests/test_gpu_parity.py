@@ -455,6 +455,41 @@ def test_reset_zeroes_state_and_restarts():
     assert torch.equal(run.params, fresh.params) and torch.equal(run.mom, fresh.mom)
 
 
+def test_checkpoint_resume_is_bit_identical():
+    # The optimizer state is the caller's momentum plus NorMuon's v in the
+    # workspace (reset() after warm-up clears exactly these, per the
+    # FixMuonLR record's change 2). k steps, a checkpoint of params,
+    # momentum and v, a fresh handle and workspace restored from it, and k
+    # more steps there must equal 2k uninterrupted steps bit for bit.
+    shapes = [(768, 768, 2, "spike"), (300, 200, 1, "spike"), (64, 64, 3, "rank8"), (1000, 700, 1, "spike"),
+              (48, 1000, 1, "gauss"), (96, 160, 1, "gauss", 1.0, 1)]
+    w = custom_workload(120, shapes, steps=4, normuon=1, lr=0.05, weight_decay=0.1)
+    k = 2
+    ref, first = GpuRun(w), GpuRun(w)
+    for t in range(k):
+        g = gen_grads(w, t)
+        for r in (ref, first):
+            r.load_grads(t, g)
+            r.step()
+    ck_p, ck_m = first.params.clone(), first.mom.clone()
+    ck_v = first.H.view(B.MUON_VIEW_V, torch.float32).clone()
+    first.H.close()
+    resumed = GpuRun(w)
+    resumed.params.copy_(ck_p)
+    resumed.mom.copy_(ck_m)
+    resumed.H.view(B.MUON_VIEW_V, torch.float32).copy_(ck_v)
+    torch.cuda.synchronize()
+    for t in range(k, 2 * k):
+        g = gen_grads(w, t)
+        for r in (ref, resumed):
+            r.load_grads(t, g)
+            r.step()
+    assert torch.equal(ref.params, resumed.params)
+    assert torch.equal(ref.mom, resumed.mom)
+    assert torch.equal(ref.H.view(B.MUON_VIEW_V, torch.float32), resumed.H.view(B.MUON_VIEW_V, torch.float32))
+    assert torch.any(ref.H.view(B.MUON_VIEW_V, torch.float32) != 0)
+
+
 def test_empty_and_all_frozen_tables_are_noops():
     w = custom_workload(107, [(64, 64, 2, "gauss", 1.0, 1)], steps=1)
     run = GpuRun(w)
