@@ -135,6 +135,27 @@ muon_status muon_workspace_bytes(const muon_matrix* table, int32_t n, const muon
 muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp,
                       void* workspace, size_t ws_bytes, int32_t device);
 
+/* Size of the library's own device workspace (64 MiB per GPU). */
+#define MUON_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* muon_init without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the handle's workspace is a file-scope device
+ * array of MUON_STATIC_WORKSPACE_BYTES inside the library, one per GPU, held
+ * from the library's first use of that GPU until the process ends. Everything
+ * else is muon_init's: the same plan, uploads and zeroing (the array keeps
+ * the previous handle's contents, so the state that must start at zero is
+ * cleared here), blocking, and the returned handle works with muon_step,
+ * muon_reset and the views as usual. No device memory is allocated and no
+ * stream or event is created: hp->stream_groups is taken as 1.
+ * Tables whose muon_workspace_bytes exceed MUON_STATIC_WORKSPACE_BYTES are
+ * rejected with MUON_E_WORKSPACE. All handles made this way on one GPU share
+ * its array: a later muon_init_static on that GPU takes it over (an earlier
+ * handle on the GPU must not be stepped afterwards), and calls on such
+ * handles that overlap in time race. */
+muon_status muon_init_static(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp,
+                             int32_t device);
+
 /* One Muon step ([P4] Muon source; [P2] change 2), enqueued on `stream`:
  * momentum + Nesterov, Frobenius normalisation, hp.ns_steps Newton–Schulz
  * iterations, optional NorMuon, and

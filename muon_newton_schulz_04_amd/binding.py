@@ -26,6 +26,7 @@ MUON_E_WORKSPACE = -7
 MUON_E_HOST = -8
 
 MUON_MAX_NS_STEPS = 16
+MUON_STATIC_WORKSPACE_BYTES = 64 << 20
 MUON_NS_BF16 = 0
 MUON_NS_FP32 = 1
 MUON_MOMENTUM_LERP = 0
@@ -115,6 +116,8 @@ _SIGS = {
                                             ctypes.POINTER(muon_hparams), ctypes.POINTER(ctypes.c_size_t)]),
     "muon_init": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(muon_matrix), ctypes.c_int32,
                                  ctypes.POINTER(muon_hparams), _P, ctypes.c_size_t, ctypes.c_int32]),
+    "muon_init_static": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(muon_matrix), ctypes.c_int32,
+                                        ctypes.POINTER(muon_hparams), ctypes.c_int32]),
     "muon_step": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_float, ctypes.c_float, _P]),
     "muon_reset": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
     "muon_destroy": (None, [_P]),
@@ -206,6 +209,14 @@ def muon_init(entries, hp: Optional[muon_hparams], workspace_ptr: int, ws_bytes:
     h = _P()
     s = load().muon_init(ctypes.byref(h), tbl, len(entries), ctypes.byref(hp) if hp is not None else None,
                          _P(workspace_ptr), ws_bytes, device)
+    return s, h
+
+
+def muon_init_static(entries, hp: Optional[muon_hparams], device: int) -> tuple:
+    tbl = _table(entries)
+    h = _P()
+    s = load().muon_init_static(ctypes.byref(h), tbl, len(entries), ctypes.byref(hp) if hp is not None else None,
+                                device)
     return s, h
 
 

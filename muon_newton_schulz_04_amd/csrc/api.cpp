@@ -191,17 +191,34 @@ muon_status muon_workspace_bytes(const muon_matrix* table, int32_t n, const muon
     });
 }
 
+// muon_init (use_static = false: the caller's workspace) and muon_init_static
+// (the library's static workspace on `device`, one stream group)
 static muon_status init_impl(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp,
-                             void* workspace, size_t ws_bytes, int32_t device) {
+                             void* workspace, size_t ws_bytes, int32_t device, bool use_static) {
     if (!out) return fail(nullptr, MUON_E_INVALID_ARG, "null handle output");
     *out = nullptr;
     std::unique_ptr<muon_handle> owner(new muon_handle());
     muon_handle* h = owner.get();
     std::string err;
+    muon_hparams hp1;
+    if (use_static) {
+        // no stream or event is created: every launch on the caller's stream
+        if (hp)
+            hp1 = *hp;
+        else
+            muon_hparams_default(&hp1);
+        hp1.stream_groups = 1;
+        hp = &hp1;
+    }
     muon_status s = muon::build_plan(table, n, hp, &h->plan, &err);
     if (s != MUON_OK) return fail(nullptr, s, err);
     const muon::Plan& P = h->plan;
-    if (P.total_bytes > 0) {
+    if (use_static) {
+        if (P.total_bytes > MUON_STATIC_WORKSPACE_BYTES)
+            return fail(nullptr, MUON_E_WORKSPACE,
+                        "table needs " + std::to_string(P.total_bytes) + " bytes of workspace; the static workspace "
+                        "holds " + std::to_string(MUON_STATIC_WORKSPACE_BYTES));
+    } else if (P.total_bytes > 0) {
         if (!workspace) {
             return fail(nullptr, MUON_E_WORKSPACE, "null workspace");
         }
@@ -234,6 +251,15 @@ static muon_status init_impl(muon_handle** out, const muon_matrix* table, int32_
     e = hipSetDevice(device);
     if (e != hipSuccess) {
         return hip_fail(nullptr, e, "hipSetDevice");
+    }
+    if (use_static) {
+        // the device address of the static array on this device (never its host-side name)
+        e = muon::static_scratch_address(device, &workspace);
+        if (e != hipSuccess) {
+            if (prev >= 0) (void)hipSetDevice(prev);
+            return hip_fail(nullptr, e, "hipGetSymbolAddress of the static workspace");
+        }
+        ws_bytes = MUON_STATIC_WORKSPACE_BYTES;
     }
     h->device = device;
     h->ws = static_cast<char*>(workspace);
@@ -275,7 +301,13 @@ static muon_status init_impl(muon_handle** out, const muon_matrix* table, int32_
 muon_status muon_init(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp, void* workspace,
                       size_t ws_bytes, int32_t device) {
     return guarded(nullptr, "muon_init",
-                   [&]() { return init_impl(out, table, n, hp, workspace, ws_bytes, device); });
+                   [&]() { return init_impl(out, table, n, hp, workspace, ws_bytes, device, false); });
+}
+
+muon_status muon_init_static(muon_handle** out, const muon_matrix* table, int32_t n, const muon_hparams* hp,
+                             int32_t device) {
+    return guarded(nullptr, "muon_init_static",
+                   [&]() { return init_impl(out, table, n, hp, nullptr, 0, device, true); });
 }
 
 static muon_status step_impl(muon_handle* h, float* params, const float* grads, float* momentum, int64_t numel,

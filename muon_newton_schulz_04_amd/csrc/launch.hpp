@@ -83,4 +83,7 @@ size_t ns_small_lds_bytes(int n_pad_max);
 // the current device (once, at init; launches do not repeat it).
 hipError_t prepare_ns_small(int n_pad_max);
 
+// Device address of the library's static workspace on `device` (current).
+hipError_t static_scratch_address(int device, void** addr);
+
 }  // namespace muon

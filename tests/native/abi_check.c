@@ -195,6 +195,21 @@ int main(void) {
         EXPECT(strlen(muon_last_error(NULL)) > 0);
     }
 
+    /* muon_init_static: the same checks, and tables beyond the static workspace */
+    {
+        muon_handle* h = (muon_handle*)1;
+        EXPECT(muon_init_static(NULL, t, 1, &hp, 0) == MUON_E_INVALID_ARG);
+        n = body(t, 12, 768); /* the 124M body needs far more than the static workspace */
+        EXPECT(muon_init_static(&h, t, n, &hp, 0) == MUON_E_WORKSPACE && h == NULL);
+        EXPECT(strstr(muon_last_error(NULL), "static workspace") != NULL);
+        n = body(t, 1, 128);
+        h = (muon_handle*)1;
+        EXPECT(muon_init_static(&h, t, n, NULL, 1000) == MUON_E_NO_DEVICE && h == NULL);
+        t[0].count = 0;
+        EXPECT(muon_init_static(&h, t, n, &hp, 0) == MUON_E_SHAPE && h == NULL);
+        t[0].count = 4;
+    }
+
     /* every entry point taking a handle rejects NULL */
     {
         float x[4] = {0, 0, 0, 0};

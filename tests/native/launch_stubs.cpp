@@ -25,5 +25,6 @@ hipError_t launch_ns_small(const LaunchCtx&, const int32_t*, int, int, const NsC
 }
 size_t ns_small_lds_bytes(int n_pad_max) { return (size_t)n_pad_max; }
 hipError_t prepare_ns_small(int) { return hipErrorNotSupported; }
+hipError_t static_scratch_address(int, void**) { return hipErrorNotSupported; }
 
 }  // namespace muon
