@@ -5,11 +5,16 @@ GPT-2-124M body (12 layers, d = 768: 48 [768,768] + 12 [768,3072] + 12
 
 Prints one JSON line. `value` is the Newton-Schulz algorithmic TFLOP/s of the
 whole step (all kernels, inputs resident in HBM); `ms_per_step` is the step
-latency. `roofline` covers the dominant kernel, timed with HIP events around
-each of its launches inside the timed region; `cpu_baseline` times the
-float64 CPU oracle on a bounded sample of the same workload.
+latency, `step_ms` its per-step mean, std, median and min. `roofline` covers
+the dominant kernel, timed with HIP events around each of its launches on its
+own stream; `cpu_baseline` times the float64 CPU oracle on a bounded sample of
+the same workload (bf16-contract and exact modes, plus one 1.5B-body layer
+extrapolated to 48). `per_config` repeats the measurement for the other four
+workloads (the tiny fp32 block, the 124M body with NorMuon, the stress batch
+and the 1.5B body, the last with one gradient set); `env` records the
+software and hardware.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-other-configs]
 """
 
 from __future__ import annotations
@@ -254,43 +259,233 @@ def trace_summary(trace_dir: str, workload: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def cpu_baseline(seconds: float) -> dict:
-    """The oracle (float64 NumPy, bf16 rounding contract) on layer 0 of the body."""
+def _oracle_layer(d: int, seed: int):
+    from workloads import custom_workload
+    return custom_workload(seed, [(d, d, 4, "spike"), (d, 4 * d, 1, "spike"), (4 * d, d, 1, "spike")])
+
+
+def _ns_alg_flops_step(layer, ns_steps: int = 5) -> float:
+    f = 0.0
+    for _gi, _ei, _k, _off, r, c in layer.submatrices():
+        m, n = min(r, c), max(r, c)
+        f += ns_steps * (m * (m + 1) * n + m * (m + 1) * m + 2 * m * m * n)
+    return f
+
+
+def _time_oracle(layer, mode: str, seconds: float, min_steps: int = 1):
+    """Full oracle steps (momentum, NS, update) on one layer until `seconds`
+    of oracle time have passed (at least min_steps); gradient generation is
+    not timed. Returns (steps, seconds)."""
     import numpy as np
 
     import oracle as O
-    from workloads import custom_workload, gen_grads, gen_params
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    d = 768
-    layer = custom_workload(1, [(d, d, 4, "spike"), (d, 4 * d, 1, "spike"), (4 * d, d, 1, "spike")])
-    orc = O.OracleMuon(layer.entries, layer.total, mode="bf16")
+    from workloads import gen_grads, gen_params
+    orc = O.OracleMuon(layer.entries, layer.total, mode=mode)
     p = gen_params(layer).astype(np.float64)
-    flops_per_step = 0.0
-    for _gi, _ei, _k, _off, r, c in layer.submatrices():
-        m, n = min(r, c), max(r, c)
-        flops_per_step += 5 * (m * (m + 1) * n + m * (m + 1) * m + 2 * m * m * n)
-    steps = 0
-    el = 0.0  # oracle time only; drawing the gradients is not timed
-    while el < seconds:
+    steps, el = 0, 0.0
+    while el < seconds or steps < min_steps:
         g = gen_grads(layer, steps)
         t1 = time.perf_counter()
         p = orc.step(p, g, lr=0.02)
         el += time.perf_counter() - t1
         steps += 1
-    return {
-        "value": flops_per_step * steps / el / 1e12,
+    return steps, el
+
+
+def cpu_baseline(seconds: float) -> dict:
+    """The oracle (float64 NumPy) timed on the host: full steps of layer 0 of
+    the 124M body in the bf16-contract mode (the reported value) and in the
+    exact mode, and one step of one layer of the 1.5B body (exact mode),
+    extrapolated to its 48 layers."""
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    layer = _oracle_layer(768, 1)
+    f_layer = _ns_alg_flops_step(layer)
+    sc, ec = _time_oracle(layer, "bf16", seconds)
+    se, ee = _time_oracle(layer, "exact", seconds * 0.5)
+    big = _oracle_layer(1600, 3)
+    sb, eb = _time_oracle(big, "exact", 0.0, min_steps=1)
+    out = {
+        "value": f_layer * sc / ec / 1e12,
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
         "sample": f"layer 0 of the 124M body (4x[768,768] + [768,3072] + [3072,768]), bf16-contract "
-                  f"float64 oracle, {steps} full step(s) incl. momentum and update, {el:.1f} s; "
+                  f"float64 oracle, {sc} full step(s) incl. momentum and update, {ec:.1f} s; "
                   f"rate = NS algorithmic FLOP / wall time",
-        "ms_per_layer_step": el / steps * 1e3,
+        "ms_per_layer_step": ec / sc * 1e3,
+        "modes": {
+            "bf16_contract": {"steps": sc, "seconds": ec, "ms_per_layer_step": ec / sc * 1e3,
+                              "tflops": f_layer * sc / ec / 1e12,
+                              "ms_per_step_12_layers_extrapolated": 12 * ec / sc * 1e3},
+            "exact": {"steps": se, "seconds": ee, "ms_per_layer_step": ee / se * 1e3,
+                      "tflops": f_layer * se / ee / 1e12,
+                      "ms_per_step_12_layers_extrapolated": 12 * ee / se * 1e3},
+        },
+        "body_1p5b": {"sample": "one layer of the 1.5B body (4x[1600,1600] + [1600,6400] + [6400,1600]), exact "
+                                "float64 oracle, one full step",
+                      "ms_per_layer_step": eb / sb * 1e3,
+                      "tflops": _ns_alg_flops_step(big) * sb / eb / 1e12,
+                      "ms_per_step_48_layers_extrapolated": 48 * eb / sb * 1e3,
+                      "note": "extrapolation: one measured layer x 48 layers"},
     }
+    return out
+
+
+def env_snapshot() -> dict:
+    """Versions and hardware of the run (GPU, ROCm, hipcc, torch, host CPU)."""
+    import platform
+    import subprocess
+
+    import numpy as np
+    import torch
+    env = {"gpu": torch.cuda.get_device_name(0) if torch.cuda.is_available() else None,
+           "torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None),
+           "python": platform.python_version(), "numpy": np.__version__, "host_cores": os.cpu_count()}
+    try:
+        props = torch.cuda.get_device_properties(0)
+        env["gpu_arch"] = getattr(props, "gcnArchName", None)
+        env["gpu_cus"] = props.multi_processor_count
+        env["gpu_mem_gib"] = round(props.total_memory / 2 ** 30, 1)
+    except Exception:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=30)
+        env["hipcc"] = " | ".join(x.strip() for x in r.stdout.splitlines() if "version" in x.lower())[:200]
+    except Exception:
+        env["hipcc"] = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            env["cpu"] = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        env["cpu"] = None
+    return env
+
+
+def _stats(xs):
+    import statistics
+    return {"mean": statistics.mean(xs), "std": statistics.stdev(xs) if len(xs) > 1 else 0.0,
+            "median": statistics.median(xs), "min": min(xs), "max": max(xs), "n": len(xs)}
+
+
+def measure(w, steps: int, warmup: int, kernel_steps: int, pool: int, stream_groups: int, events: bool = True):
+    """Time workload w on cuda:0 through the C ABI.
+
+    Timed pass: the shipped stream-group schedule, a HIP event on the
+    caller's stream before the first step and after every step (each step
+    joins the caller's stream at its end, and the next starts after it), so
+    per-step times and the mean come from the same run. Kernel pass: the same
+    steps with every launch on one stream, each launch bracketed by the
+    library's own HIP events on that stream (per-kernel averages, roofline).
+    Inputs are resident in HBM before timing; `pool` gradient sets are
+    cycled."""
+    import numpy as np
+    import torch
+
+    from muon_newton_schulz_04_amd import binding as B
+    from workloads import gen_grads, gen_params
+
+    hpkw = dict(momentum=w.momentum, nesterov=w.nesterov, ns_steps=w.ns_steps, precision=w.ns_precision,
+                normuon=w.normuon, normuon_beta2=w.normuon_beta2, normuon_eps=w.normuon_eps,
+                weight_decay=w.weight_decay)
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    params = torch.from_numpy(gen_params(w)).to(dev)
+    grads = [torch.from_numpy(gen_grads(w, t)).to(dev) for t in range(pool)]
+    t_gen = time.perf_counter() - t_gen
+    mom = torch.zeros(w.total, dtype=torch.float32, device=dev)
+    H = B.MuonHandle(w.entries, B.make_hparams(**hpkw, stream_groups=stream_groups))
+    work = B.muon_work_stats(H.h)
+    stream = torch.cuda.current_stream(dev)
+    print(f"# workload {w.name}: {w.num_matrices} matrices, {w.total} elements, workspace "
+          f"{H.ws_bytes / 2**20:.0f} MiB, inputs drawn in {t_gen:.1f} s", file=sys.stderr, flush=True)
+    for t in range(warmup):
+        H.step(params, grads[t % pool], mom, w.lr)
+    H.reset(mom)  # warm-up dirtied the optimizer state
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for t in range(steps):
+        H.step(params, grads[t % pool], mom, w.lr)
+        ev[t + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = [ev[t].elapsed_time(ev[t + 1]) for t in range(steps)]
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    ns_flops = sum(work.flops[k] for k in (B.MUON_KERNEL_GRAM, B.MUON_KERNEL_POLY, B.MUON_KERNEL_UPDATE,
+                                            B.MUON_KERNEL_NS_SMALL))
+    fp32 = w.ns_precision == "fp32"
+    peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    res = {"workload": w.name, "steps": steps, "warmup": warmup, "grad_sets": pool, "ms_per_step": ms,
+           "step_ms": _stats(per_step), "wall_s": wall, "ns_alg_gflop_per_step": ns_flops / 1e9,
+           "ns_tflops_step": ns_flops / (ms * 1e-3) / 1e12, "pct_peak_step": ns_flops / (ms * 1e-3) / 1e12 / peak * 100,
+           "peak_tflops": peak, "dtype": "fp32" if fp32 else "bf16", "elements": w.total,
+           "matrices": w.num_matrices}
+    del H
+    kernels = {}
+    if events and kernel_steps > 0:
+        H1 = B.MuonHandle(w.entries, B.make_hparams(**hpkw, stream_groups=1))
+        for t in range(min(warmup, 3)):
+            H1.step(params, grads[t % pool], mom, w.lr)
+        torch.cuda.synchronize()
+        B.muon_profile_enable(H1.h, 1)
+        for t in range(kernel_steps):
+            H1.step(params, grads[t % pool], mom, w.lr)
+        torch.cuda.synchronize()
+        B.muon_profile_enable(H1.h, 0)
+        work1 = B.muon_work_stats(H1.h)
+        for k, name in enumerate(B.KERNEL_NAMES):
+            s, n, tot = B.muon_profile_read(H1.h, k, 0)
+            if n == 0:
+                continue
+            per_launch_ms = tot / n
+            entry = {"launches": n, "avg_ms": per_launch_ms, "ms_per_step": tot / kernel_steps}
+            lps = work1.launches[k]
+            if work1.flops[k] > 0:
+                entry["tflops"] = work1.flops[k] / lps / (per_launch_ms * 1e-3) / 1e12
+                entry["pct_peak"] = entry["tflops"] / peak * 100
+            if work1.bytes[k] > 0:
+                entry["gbs"] = work1.bytes[k] / lps / (per_launch_ms * 1e-3) / 1e9
+                entry["pct_hbm_peak"] = entry["gbs"] / PEAK_HBM_GBS * 100
+            kernels[name] = entry
+        B.muon_profile_read(H1.h, 0, 1)
+        ns_ms = sum(kernels.get(k, {}).get("ms_per_step", 0.0) for k in ("gram", "poly", "update", "ns_small"))
+        res["ns_tflops_kernels"] = ns_flops / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None
+        res["kernel_pass_steps"] = kernel_steps
+        if kernels:
+            dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+            kidx = B.KERNEL_NAMES.index(dom)
+            e = kernels[dom]
+            if work1.flops[kidx] > 0:
+                rf = {"bound": "mfma", "achieved": e["tflops"], "peak": peak, "unit": "TFLOP/s",
+                      "frac": e["tflops"] / peak, "alg_per_launch": work1.flops[kidx] / work1.launches[kidx]}
+            else:
+                rf = {"bound": "hbm", "achieved": e["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": e["gbs"] / PEAK_HBM_GBS, "alg_per_launch": work1.bytes[kidx] / work1.launches[kidx]}
+            rf["kernel"] = dom
+            rf["avg_launch_ms"] = e["avg_ms"]
+            rf["traffic"] = _traffic(dom, w.name)
+            res["roofline"] = rf
+        del H1
+    res["kernels"] = kernels
+    assert np.isfinite(params[:1000].cpu().numpy()).all()
+    del params, grads, mom
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+# the other workloads: (config id, timed steps, kernel-pass steps, gradient sets)
+OTHER_CONFIGS = ((0, 50, 20, 4), (2, 50, 20, 4), (4, 50, 20, 4), (3, 10, 3, 1))
 
 
 def main() -> int:
@@ -299,9 +494,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1, help="workload id (1 = GPT-2-124M body)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="do not time kernels with events")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="measure only the headline workload (no per-config section)")
     ap.add_argument("--stream-groups", type=int, default=3, help="stream groups of the timed pass (1 .. 4)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB once per pass (HBM counter calibration)")
@@ -347,115 +544,31 @@ def main() -> int:
               "multi-GPU step is not part of it.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
-    from muon_newton_schulz_04_amd import binding as B
-    from workloads import gen_grads, gen_params, get_workload
+    from workloads import get_workload
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     w = get_workload(args.config)
-    hpkw = dict(momentum=w.momentum, nesterov=w.nesterov, ns_steps=w.ns_steps, precision=w.ns_precision,
-                normuon=w.normuon, normuon_beta2=w.normuon_beta2, normuon_eps=w.normuon_eps,
-                weight_decay=w.weight_decay)
-    # the step as shipped: tiled matrices split over stream groups
-    H = B.MuonHandle(w.entries, B.make_hparams(**hpkw, stream_groups=args.stream_groups))
-    work = B.muon_work_stats(H.h)
-    dev = torch.device("cuda:0")
-    params = torch.from_numpy(gen_params(w)).to(dev)
-    mom = torch.zeros(w.total, dtype=torch.float32, device=dev)
-    pool = [torch.from_numpy(gen_grads(w, t)).to(dev) for t in range(GRAD_POOL)]
-    stream = torch.cuda.current_stream(dev)
-    print(f"# workload {w.name}: {w.num_matrices} matrices, {w.total} elements, "
-          f"workspace {H.ws_bytes / 2**20:.0f} MiB", file=sys.stderr, flush=True)
-
-    for t in range(args.warmup):
-        H.step(params, pool[t % GRAD_POOL], mom, w.lr)
-    H.reset(mom)  # warm-up dirtied the optimizer state
-    torch.cuda.synchronize()
-
-    # timed region: whole steps, no per-launch events (they would serialise
-    # the stream groups)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for t in range(args.steps):
-        H.step(params, pool[t % GRAD_POOL], mom, w.lr)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / args.steps
-
-    # kernel pass: every launch on one stream, each bracketed by HIP events on
-    # that stream, so each kernel is timed with the GPU to itself (the
-    # per-kernel table and the roofline come from here)
-    H1 = None
-    if not args.no_events:
-        del H
-        H1 = B.MuonHandle(w.entries, B.make_hparams(**hpkw, stream_groups=1))
-        for t in range(min(args.warmup, 3)):
-            H1.step(params, pool[t % GRAD_POOL], mom, w.lr)
-        torch.cuda.synchronize()
-        B.muon_profile_enable(H1.h, 1)
-        for t in range(args.steps):
-            H1.step(params, pool[t % GRAD_POOL], mom, w.lr)
-        torch.cuda.synchronize()
-        B.muon_profile_enable(H1.h, 0)
-        work1 = B.muon_work_stats(H1.h)
-    assert np.isfinite(params[:1000].cpu().numpy()).all()
-
-    ns_flops = (work.flops[B.MUON_KERNEL_GRAM] + work.flops[B.MUON_KERNEL_POLY] + work.flops[B.MUON_KERNEL_UPDATE]
-                + work.flops[B.MUON_KERNEL_NS_SMALL])
-    value = ns_flops / (ms * 1e-3) / 1e12
+    head = measure(w, args.steps, args.warmup, 0 if args.no_events else args.steps, GRAD_POOL, args.stream_groups,
+                   events=not args.no_events)
+    others = {}
+    if not args.no_other_configs and args.config == 1:
+        for cid, st, kst, pool in OTHER_CONFIGS:
+            wo = get_workload(cid)
+            others[wo.name] = measure(wo, st, min(args.warmup, 10), 0 if args.no_events else kst, pool,
+                                      args.stream_groups, events=not args.no_events)
     fp32 = w.ns_precision == "fp32"
-    peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
-
-    kernels = {}
-    if H1 is not None:
-        for k, name in enumerate(B.KERNEL_NAMES):
-            s, n, tot = B.muon_profile_read(H1.h, k, 0)
-            if n == 0:
-                continue
-            per_launch_ms = tot / n
-            entry = {"launches": n, "avg_ms": per_launch_ms, "ms_per_step": tot / args.steps}
-            lps = work1.launches[k]
-            if work1.flops[k] > 0:
-                entry["tflops"] = work1.flops[k] / lps / (per_launch_ms * 1e-3) / 1e12
-            if work1.bytes[k] > 0:
-                entry["gbs"] = work1.bytes[k] / lps / (per_launch_ms * 1e-3) / 1e9
-            kernels[name] = entry
-        B.muon_profile_read(H1.h, 0, 1)
-    ns_ms = sum(kernels.get(k, {}).get("ms_per_step", 0.0) for k in ("gram", "poly", "update", "ns_small"))
-    roofline = None
-    if kernels:
-        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-        kidx = B.KERNEL_NAMES.index(dom)
-        e = kernels[dom]
-        if work1.flops[kidx] > 0:
-            achieved = e["tflops"]
-            roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                        "frac": achieved / peak, "kernel": dom,
-                        "alg_per_launch": work1.flops[kidx] / work1.launches[kidx]}
-        else:
-            achieved = e["gbs"]
-            roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": achieved / PEAK_HBM_GBS, "kernel": dom,
-                        "alg_per_launch": work1.bytes[kidx] / work1.launches[kidx]}
-        roofline["avg_launch_ms"] = e["avg_ms"]
-        roofline["traffic"] = _traffic(dom, w.name)
-
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": head["ns_tflops_step"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -464,15 +577,17 @@ def main() -> int:
         "config": {"workload": w.name, "layers": len(w.entries) // 3 if args.config in (1, 2, 3) else None,
                    "matrices": w.num_matrices, "elements": w.total, "ns_steps": w.ns_steps,
                    "ns_precision": w.ns_precision, "normuon": w.normuon, "parallelism": "single GPU"},
-        "ns_alg_gflop_per_step": ns_flops / 1e9,
-        "ns_tflops_kernels": (ns_flops / (ns_ms * 1e-3) / 1e12) if ns_ms > 0 else None,
-        "pct_bf16_peak_step": value / PEAK_BF16_TFLOPS * 100.0,
-        "roofline": roofline,
-        "kernels": kernels,
+        "step_ms": head["step_ms"],
+        "ns_alg_gflop_per_step": head["ns_alg_gflop_per_step"],
+        "ns_tflops_kernels": head.get("ns_tflops_kernels"),
+        "pct_bf16_peak_step": head["ns_tflops_step"] / PEAK_BF16_TFLOPS * 100.0,
+        "roofline": head.get("roofline"),
+        "kernels": head["kernels"],
         "kernels_pass": "a second pass of the same steps with every launch on one stream (stream_groups=1), "
                         "each timed with HIP events; the timed region above runs the shipped stream-group "
                         "schedule without per-launch events",
-        "wall_s": wall,
+        "per_config": others,
+        "wall_s": head["wall_s"],
         "device": torch.cuda.get_device_name(0),
         "source_hash": _kernel_source_hash(),
     }
@@ -480,6 +595,7 @@ def main() -> int:
         copy_calibration()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    out["env"] = env_snapshot()
     print(json.dumps(out), flush=True)
     return 0
 
