@@ -10,8 +10,11 @@ namespace muon {
 // canonical buffer is padded to a multiple of its bucket's T in both
 // dimensions (zero-filled padding keeps Newton–Schulz exact on the valid
 // block, so the GEMM kernels carry no bounds checks). Elementwise kernels
-// work on 64 x 64 tiles of the padded canonical frame.
+// work on 64 x 64 tiles of the canonical frame for matrices stored with rows
+// > cols (transposed through LDS), and on runs of kEwLinear consecutive
+// stored elements for the others, whose canonical frame is the stored one.
 constexpr int kEwTile = 64;
+constexpr int kEwLinear = 4096;
 constexpr int kThreads = 256;
 // bf16 matrices with m_pad = 64 and n_pad <= kSmallMaxNPad run every
 // Newton–Schulz iteration in one workgroup (X, A, P resident in LDS).
@@ -32,7 +35,7 @@ struct MatDesc {
     int32_t row_off;      // offset into the per-row NorMuon arrays (v, f)
     int32_t ew_start;     // first elementwise tile (index into the momentum partials)
     int32_t ew_count;     // number of elementwise tiles
-    int32_t ew_tiles_n;   // elementwise tiles per canonical row band (ceil(n / 64))
+    int32_t ew_tiles_n;   // transposed: 64 x 64 tiles per canonical row band (ceil(n / 64)); else 0
     float lr_mul, wd_mul, shape_scale;
     int32_t vec_ok;       // stored rows start 16-byte aligned (float4 access legal)
 };

@@ -8,12 +8,15 @@
 // [P2] "2025-10-27_FixMuonLR" analysis, change 2 (lerp momentum buffer,
 // NorMuon per-lane second moment along the longer dimension).
 //
-// All kernels work on 64 x 64 tiles of a matrix's canonical frame (rows <=
-// cols), over its valid block rounded up to whole tiles; the momentum kernel
-// writes zeros into the padding inside those tiles (the rest of the X~
-// padding is zeroed once when the handle is created). Matrices stored with rows > cols are transposed through
-// LDS so that both the stored-frame and canonical-frame accesses stay
-// coalesced.
+// Matrices stored with rows > cols are transposed into their canonical frame
+// (rows <= cols) through LDS, in 64 x 64 tiles over the valid block rounded
+// up to whole tiles, so that both the stored-frame and the canonical-frame
+// accesses stay coalesced; the momentum kernel writes zeros into the padding
+// inside those tiles. For the other matrices the two frames coincide and a
+// tile is a run of kEwLinear (4096) consecutive stored elements, which the
+// kernels stream like a flat copy: every wave instruction covers 1 KB of one
+// fp32 stream, and a workgroup 16 KB. The X~ padding that no tile writes is
+// zeroed once when the handle is created.
 
 #include "kernel_common.hpp"
 #include "launch.hpp"
@@ -102,11 +105,139 @@ __device__ __forceinline__ void load_x4<float>(const float* src, float* v) {
     v[3] = w.w;
 }
 
+template <typename XT>
+__device__ __forceinline__ void store_x1(XT* dst, float v) {
+    *dst = (XT)v;  // bf16: round to nearest even, as pack_bf16x2
+}
+
+template <typename XT>
+__device__ __forceinline__ float load_x1(const XT* src) {
+    return (float)*src;
+}
+
+// Element e (0 <= e < R C < 2^30) of an untransposed matrix is canonical
+// (e / C, e % C).
+__device__ __forceinline__ void split_index(int e, int C, int& i, int& j) {
+    i = (int)((unsigned)e / (unsigned)C);
+    j = e - i * C;
+}
+
+// Momentum over run lt of an untransposed matrix; returns this thread's sum
+// of u^2. Thread t owns the float4 groups at 4 t + 1024 p, p = 0 .. 3.
+template <typename XT>
+__device__ __forceinline__ float momentum_run(const MatDesc& d, int lt, const float* __restrict__ grads,
+                                              float* __restrict__ mom, XT* __restrict__ xt, const MomParams& P) {
+    const int total = d.R * d.C;
+    const int e0 = lt * kEwLinear + 4 * (int)threadIdx.x;
+    float ssq = 0.0f;
+    if (d.vec_ok) {
+        // C % 4 == 0: a float4 group never crosses a row, and total % 4 == 0
+        const bool full = (lt + 1) * kEwLinear <= total;
+        float4 g4[4], m4[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int e = e0 + p * 4 * kThreads;
+            if (full || e < total) {
+                g4[p] = ntld4(grads + d.p_off + e);
+                m4[p] = ntld4(mom + d.p_off + e);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int e = e0 + p * 4 * kThreads;
+            if (full || e < total) {
+                float u[4];
+                u[0] = mom_update(g4[p].x, m4[p].x, P);
+                u[1] = mom_update(g4[p].y, m4[p].y, P);
+                u[2] = mom_update(g4[p].z, m4[p].z, P);
+                u[3] = mom_update(g4[p].w, m4[p].w, P);
+                ntst4(mom + d.p_off + e, m4[p]);
+                ssq = fmaf(u[0], u[0], ssq);
+                ssq = fmaf(u[1], u[1], ssq);
+                ssq = fmaf(u[2], u[2], ssq);
+                ssq = fmaf(u[3], u[3], ssq);
+                int i, j;
+                split_index(e, d.C, i, j);
+                store_x4<XT>(xt + d.x_off + (int64_t)i * d.n_pad + j, u[0], u[1], u[2], u[3]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = e0 + p * 4 * kThreads + k;
+                if (e < total) {
+                    float mv = mom[d.p_off + e];
+                    const float u = mom_update(grads[d.p_off + e], mv, P);
+                    mom[d.p_off + e] = mv;
+                    ssq = fmaf(u, u, ssq);
+                    int i, j;
+                    split_index(e, d.C, i, j);
+                    store_x1<XT>(xt + d.x_off + (int64_t)i * d.n_pad + j, u);
+                }
+            }
+    }
+    return ssq;
+}
+
+// Parameter update over run lt of an untransposed matrix (same thread layout).
+template <typename XT>
+__device__ __forceinline__ void apply_run(const MatDesc& d, int lt, const XT* __restrict__ xo,
+                                          const float* __restrict__ fr, float* __restrict__ params, float decay,
+                                          float coef0) {
+    const int total = d.R * d.C;
+    const int e0 = lt * kEwLinear + 4 * (int)threadIdx.x;
+    if (d.vec_ok) {
+        const bool full = (lt + 1) * kEwLinear <= total;
+        float x[4][4];
+        float4 p4[4];
+        float coef[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int e = e0 + p * 4 * kThreads;
+            if (full || e < total) {
+                int i, j;
+                split_index(e, d.C, i, j);
+                load_x4<XT>(xo + d.x_off + (int64_t)i * d.n_pad + j, x[p]);
+                p4[p] = ntld4(params + d.p_off + e);
+                coef[p] = fr ? coef0 * fr[d.row_off + i] : coef0;
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int e = e0 + p * 4 * kThreads;
+            if (full || e < total) {
+                p4[p].x = fmaf(-coef[p], x[p][0], p4[p].x * decay);
+                p4[p].y = fmaf(-coef[p], x[p][1], p4[p].y * decay);
+                p4[p].z = fmaf(-coef[p], x[p][2], p4[p].z * decay);
+                p4[p].w = fmaf(-coef[p], x[p][3], p4[p].w * decay);
+                ntst4(params + d.p_off + e, p4[p]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = e0 + p * 4 * kThreads + k;
+                if (e < total) {
+                    int i, j;
+                    split_index(e, d.C, i, j);
+                    const float xv = load_x1<XT>(xo + d.x_off + (int64_t)i * d.n_pad + j);
+                    const float coef = fr ? coef0 * fr[d.row_off + i] : coef0;
+                    params[d.p_off + e] = fmaf(-coef, xv, params[d.p_off + e] * decay);
+                }
+            }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // K1: momentum + Nesterov + cast into the canonical Newton–Schulz input,
 // and one deterministic sum of u^2 per tile.
-// Thread layout in a 64 x 64 tile: 16 column groups of 4 x 16 row lanes,
-// four passes of 16 rows.
+// Transposed matrices: a 64 x 64 canonical tile is read as stored rows (16
+// column groups of 4 x 16 row lanes, four passes of 16 rows) and written to
+// X~ through LDS.
 // ---------------------------------------------------------------------------
 template <typename XT>
 __global__ __launch_bounds__(kThreads) void k_momentum(const MatDesc* __restrict__ mats,
@@ -119,24 +250,24 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MatDesc* __restrict
     const int tile = tile0 + blockIdx.x;
     const int mi = ew_map[tile];
     const MatDesc d = mats[mi];
-    const TileCoord tc = decode_tile(d, tile, mi);
     const int tid = threadIdx.x;
+    if (!d.transposed) {
+        const float t = block_sum_256(momentum_run<XT>(d, tile - d.ew_start, grads, mom, xt, P), red);
+        if (tid == 0) partials[tile] = t;
+        return;
+    }
+    // canonical (i, j) == stored (j, i): stored rows r = j0 + rl, columns c = i0 + cg .. +3
+    const TileCoord tc = decode_tile(d, tile, mi);
     const int cg = (tid & 15) * 4;
     const int rg = tid >> 4;
     float ssq = 0.0f;
-    // interior tile with 16-byte aligned rows: all four passes' loads go out
-    // before the first is used (the general path below waits pass by pass)
-    const bool interior = d.vec_ok && tc.i0 + TS <= d.m && tc.j0 + TS <= d.n;
-
-    if (interior) {
-        // canonical (i, j) is stored (i, j), or (j, i) when transposed; the
-        // stored-frame rows r0 + rg + 16 p, columns c0 + cg .. +3 are read
-        const int r0 = d.transposed ? tc.j0 : tc.i0;
-        const int c0 = d.transposed ? tc.i0 : tc.j0;
+    if (d.vec_ok && tc.i0 + TS <= d.m && tc.j0 + TS <= d.n) {
+        // interior tile with 16-byte aligned rows: all four passes' loads go
+        // out before the first is used
         float4 g4[4], m4[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int64_t base = d.p_off + (int64_t)(r0 + rg + 16 * p) * d.C + c0 + cg;
+            const int64_t base = d.p_off + (int64_t)(tc.j0 + rg + 16 * p) * d.C + tc.i0 + cg;
             g4[p] = ntld4(grads + base);
             m4[p] = ntld4(mom + base);
         }
@@ -147,67 +278,14 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MatDesc* __restrict
             u[1] = mom_update(g4[p].y, m4[p].y, P);
             u[2] = mom_update(g4[p].z, m4[p].z, P);
             u[3] = mom_update(g4[p].w, m4[p].w, P);
-            ntst4(mom + d.p_off + (int64_t)(r0 + rg + 16 * p) * d.C + c0 + cg, m4[p]);
-            if (!d.transposed) {
-                ssq = fmaf(u[0], u[0], ssq);
-                ssq = fmaf(u[1], u[1], ssq);
-                ssq = fmaf(u[2], u[2], ssq);
-                ssq = fmaf(u[3], u[3], ssq);
-                store_x4<XT>(xt + d.x_off + (int64_t)(tc.i0 + rg + 16 * p) * d.n_pad + tc.j0 + cg, u[0], u[1], u[2],
-                             u[3]);
-            } else {
+            ntst4(mom + d.p_off + (int64_t)(tc.j0 + rg + 16 * p) * d.C + tc.i0 + cg, m4[p]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ssq = fmaf(u[e], u[e], ssq);
-                    lds[cg + e][rg + 16 * p] = u[e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                ssq = fmaf(u[e], u[e], ssq);
+                lds[cg + e][rg + 16 * p] = u[e];
             }
-        }
-        if (d.transposed) {
-            __syncthreads();
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int il = rg + 16 * p;
-                store_x4<XT>(xt + d.x_off + (int64_t)(tc.i0 + il) * d.n_pad + tc.j0 + cg, lds[il][cg],
-                             lds[il][cg + 1], lds[il][cg + 2], lds[il][cg + 3]);
-            }
-        }
-    } else if (!d.transposed) {
-        // canonical (i, j) == stored (i, j)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int i = tc.i0 + rg + 16 * p;
-            const int j = tc.j0 + cg;
-            float u[4] = {0.f, 0.f, 0.f, 0.f};
-            if (i < d.m) {
-                const int64_t base = d.p_off + (int64_t)i * d.C + j;
-                if (d.vec_ok && j + 3 < d.n) {
-                    const float4 g4 = ntld4(grads + base);
-                    float4 m4 = ntld4(mom + base);
-                    u[0] = mom_update(g4.x, m4.x, P);
-                    u[1] = mom_update(g4.y, m4.y, P);
-                    u[2] = mom_update(g4.z, m4.z, P);
-                    u[3] = mom_update(g4.w, m4.w, P);
-                    ntst4(mom + base, m4);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (j + e < d.n) {
-                            float mv = mom[base + e];
-                            u[e] = mom_update(grads[base + e], mv, P);
-                            mom[base + e] = mv;
-                        }
-                    }
-                }
-            }
-            ssq = fmaf(u[0], u[0], ssq);
-            ssq = fmaf(u[1], u[1], ssq);
-            ssq = fmaf(u[2], u[2], ssq);
-            ssq = fmaf(u[3], u[3], ssq);
-            store_x4<XT>(xt + d.x_off + (int64_t)i * d.n_pad + j, u[0], u[1], u[2], u[3]);
         }
     } else {
-        // canonical (i, j) == stored (j, i); stored rows r = j0.., cols c = i0..
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int rl = rg + 16 * p;
@@ -241,15 +319,13 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MatDesc* __restrict
                 lds[cg + e][rl] = u[e];
             }
         }
-        __syncthreads();
+    }
+    __syncthreads();
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int il = rg + 16 * p;
-            const int i = tc.i0 + il;
-            const int j = tc.j0 + cg;
-            store_x4<XT>(xt + d.x_off + (int64_t)i * d.n_pad + j, lds[il][cg], lds[il][cg + 1],
-                         lds[il][cg + 2], lds[il][cg + 3]);
-        }
+    for (int p = 0; p < 4; ++p) {
+        const int il = rg + 16 * p;
+        store_x4<XT>(xt + d.x_off + (int64_t)(tc.i0 + il) * d.n_pad + tc.j0 + cg, lds[il][cg], lds[il][cg + 1],
+                     lds[il][cg + 2], lds[il][cg + 3]);
     }
     const float t = block_sum_256(ssq, red);
     if (tid == 0) partials[tile] = t;
@@ -258,6 +334,8 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MatDesc* __restrict
 // ---------------------------------------------------------------------------
 // K6: p <- p (1 - lr lr_mul wd wd_mul) - lr lr_mul shape_scale f_row O
 // (f_row = NorMuon factor of the canonical row, 1 without NorMuon).
+// Transposed matrices: canonical rows of O are read, turned through LDS, and
+// applied to stored rows.
 // ---------------------------------------------------------------------------
 template <typename XT>
 __global__ __launch_bounds__(kThreads) void k_apply(const MatDesc* __restrict__ mats,
@@ -268,128 +346,90 @@ __global__ __launch_bounds__(kThreads) void k_apply(const MatDesc* __restrict__ 
     const int tile = tile0 + blockIdx.x;
     const int mi = ew_map[tile];
     const MatDesc d = mats[mi];
+    const float lrm = lr * d.lr_mul;
+    const float decay = 1.0f - lrm * wd * d.wd_mul;
+    const float coef0 = lrm * d.shape_scale;
+    if (!d.transposed) {
+        apply_run<XT>(d, tile - d.ew_start, xo, fr, params, decay, coef0);
+        return;
+    }
     const TileCoord tc = decode_tile(d, tile, mi);
     if (tc.i0 >= d.m || tc.j0 >= d.n) return;  // tile lies wholly in the padding
     const int tid = threadIdx.x;
     const int cg = (tid & 15) * 4;
     const int rg = tid >> 4;
-    const float lrm = lr * d.lr_mul;
-    const float decay = 1.0f - lrm * wd * d.wd_mul;
-    const float coef0 = lrm * d.shape_scale;
 
     if (d.vec_ok && tc.i0 + TS <= d.m && tc.j0 + TS <= d.n) {
         // interior tile with 16-byte aligned rows: every load of the tile
         // goes out before the first is used
         float x[4][4];
         float4 p4[4];
-        const int r0 = d.transposed ? tc.j0 : tc.i0;
-        const int c0 = d.transposed ? tc.i0 : tc.j0;
-        // NorMuon row factors: of the canonical rows i0 + rg + 16 p, or (transposed)
-        // of the canonical rows i0 + cg + e that are this thread's stored columns
-        float fv[4] = {1.f, 1.f, 1.f, 1.f};
+        // NorMuon row factors of the canonical rows i0 + cg + e (this thread's
+        // stored columns)
+        float coef[4] = {coef0, coef0, coef0, coef0};
         if (fr) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) fv[q] = fr[d.row_off + tc.i0 + (d.transposed ? cg + q : rg + 16 * q)];
+            for (int e = 0; e < 4; ++e) coef[e] = coef0 * fr[d.row_off + tc.i0 + cg + e];
         }
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             load_x4<XT>(xo + d.x_off + (int64_t)(tc.i0 + rg + 16 * p) * d.n_pad + tc.j0 + cg, x[p]);
-            p4[p] = ntld4(params + d.p_off + (int64_t)(r0 + rg + 16 * p) * d.C + c0 + cg);
+            p4[p] = ntld4(params + d.p_off + (int64_t)(tc.j0 + rg + 16 * p) * d.C + tc.i0 + cg);
         }
-        if (!d.transposed) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int i = tc.i0 + rg + 16 * p;
-                const float coef = fr ? coef0 * fv[p] : coef0;
-                p4[p].x = fmaf(-coef, x[p][0], p4[p].x * decay);
-                p4[p].y = fmaf(-coef, x[p][1], p4[p].y * decay);
-                p4[p].z = fmaf(-coef, x[p][2], p4[p].z * decay);
-                p4[p].w = fmaf(-coef, x[p][3], p4[p].w * decay);
-                ntst4(params + d.p_off + (int64_t)i * d.C + tc.j0 + cg, p4[p]);
-            }
-        } else {
-            // O rows (canonical) through LDS to stored rows
+        for (int p = 0; p < 4; ++p)
 #pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) lds[cg + e][rg + 16 * p] = x[p][e];
-            float coef[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) coef[e] = fr ? coef0 * fv[e] : coef0;
-            __syncthreads();
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int rl = rg + 16 * p;
-                p4[p].x = fmaf(-coef[0], lds[rl][cg], p4[p].x * decay);
-                p4[p].y = fmaf(-coef[1], lds[rl][cg + 1], p4[p].y * decay);
-                p4[p].z = fmaf(-coef[2], lds[rl][cg + 2], p4[p].z * decay);
-                p4[p].w = fmaf(-coef[3], lds[rl][cg + 3], p4[p].w * decay);
-                ntst4(params + d.p_off + (int64_t)(tc.j0 + rl) * d.C + tc.i0 + cg, p4[p]);
-            }
-        }
-    } else if (!d.transposed) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int i = tc.i0 + rg + 16 * p;
-            const int j = tc.j0 + cg;
-            if (i >= d.m) continue;
-            float x[4];
-            load_x4<XT>(xo + d.x_off + (int64_t)i * d.n_pad + j, x);
-            const float coef = fr ? coef0 * fr[d.row_off + i] : coef0;
-            const int64_t base = d.p_off + (int64_t)i * d.C + j;
-            if (d.vec_ok && j + 3 < d.n) {
-                float4 p4 = ntld4(params + base);
-                p4.x = fmaf(-coef, x[0], p4.x * decay);
-                p4.y = fmaf(-coef, x[1], p4.y * decay);
-                p4.z = fmaf(-coef, x[2], p4.z * decay);
-                p4.w = fmaf(-coef, x[3], p4.w * decay);
-                ntst4(params + base, p4);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (j + e < d.n) params[base + e] = fmaf(-coef, x[e], params[base + e] * decay);
-            }
-        }
-    } else {
-        // read canonical rows (i = stored column), write stored rows
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int il = rg + 16 * p;
-            const int i = tc.i0 + il;
-            const int j = tc.j0 + cg;
-            float x[4];
-            load_x4<XT>(xo + d.x_off + (int64_t)i * d.n_pad + j, x);
-            lds[cg][il] = x[0];
-            lds[cg + 1][il] = x[1];
-            lds[cg + 2][il] = x[2];
-            lds[cg + 3][il] = x[3];
-        }
+            for (int e = 0; e < 4; ++e) lds[cg + e][rg + 16 * p] = x[p][e];
         __syncthreads();
-        float coef[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = tc.i0 + cg + e;
-            coef[e] = (fr && c < d.C) ? coef0 * fr[d.row_off + c] : coef0;
-        }
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int rl = rg + 16 * p;
-            const int r = tc.j0 + rl;
-            const int c = tc.i0 + cg;
-            if (r >= d.R) continue;
-            const int64_t base = d.p_off + (int64_t)r * d.C + c;
-            if (d.vec_ok && c + 3 < d.C) {
-                float4 p4 = ntld4(params + base);
-                p4.x = fmaf(-coef[0], lds[rl][cg], p4.x * decay);
-                p4.y = fmaf(-coef[1], lds[rl][cg + 1], p4.y * decay);
-                p4.z = fmaf(-coef[2], lds[rl][cg + 2], p4.z * decay);
-                p4.w = fmaf(-coef[3], lds[rl][cg + 3], p4.w * decay);
-                ntst4(params + base, p4);
-            } else {
+            p4[p].x = fmaf(-coef[0], lds[rl][cg], p4[p].x * decay);
+            p4[p].y = fmaf(-coef[1], lds[rl][cg + 1], p4[p].y * decay);
+            p4[p].z = fmaf(-coef[2], lds[rl][cg + 2], p4[p].z * decay);
+            p4[p].w = fmaf(-coef[3], lds[rl][cg + 3], p4[p].w * decay);
+            ntst4(params + d.p_off + (int64_t)(tc.j0 + rl) * d.C + tc.i0 + cg, p4[p]);
+        }
+        return;
+    }
+    // read canonical rows (i = stored column), write stored rows
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (c + e < d.C) params[base + e] = fmaf(-coef[e], lds[rl][cg + e], params[base + e] * decay);
-            }
+    for (int p = 0; p < 4; ++p) {
+        const int il = rg + 16 * p;
+        const int i = tc.i0 + il;
+        const int j = tc.j0 + cg;
+        float x[4];
+        load_x4<XT>(xo + d.x_off + (int64_t)i * d.n_pad + j, x);
+        lds[cg][il] = x[0];
+        lds[cg + 1][il] = x[1];
+        lds[cg + 2][il] = x[2];
+        lds[cg + 3][il] = x[3];
+    }
+    __syncthreads();
+    float coef[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int c = tc.i0 + cg + e;
+        coef[e] = (fr && c < d.C) ? coef0 * fr[d.row_off + c] : coef0;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int rl = rg + 16 * p;
+        const int r = tc.j0 + rl;
+        const int c = tc.i0 + cg;
+        if (r >= d.R) continue;
+        const int64_t base = d.p_off + (int64_t)r * d.C + c;
+        if (d.vec_ok && c + 3 < d.C) {
+            float4 p4 = ntld4(params + base);
+            p4.x = fmaf(-coef[0], lds[rl][cg], p4.x * decay);
+            p4.y = fmaf(-coef[1], lds[rl][cg + 1], p4.y * decay);
+            p4.z = fmaf(-coef[2], lds[rl][cg + 2], p4.z * decay);
+            p4.w = fmaf(-coef[3], lds[rl][cg + 3], p4.w * decay);
+            ntst4(params + base, p4);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c + e < d.C) params[base + e] = fmaf(-coef[e], lds[rl][cg + e], params[base + e] * decay);
         }
     }
 }
@@ -468,25 +508,25 @@ __global__ __launch_bounds__(kThreads) void k_zero_momentum(const MatDesc* __res
     const int tile = blockIdx.x;
     const int mi = ew_map[tile];
     const MatDesc d = mats[mi];
+    const int tid = threadIdx.x;
+    if (!d.transposed) {
+        const int total = d.R * d.C;
+        const int e0 = (tile - d.ew_start) * kEwLinear;
+        for (int e = e0 + tid; e < e0 + kEwLinear && e < total; e += kThreads) mom[d.p_off + e] = 0.f;
+        return;
+    }
     const TileCoord tc = decode_tile(d, tile, mi);
     if (tc.i0 >= d.m || tc.j0 >= d.n) return;
-    const int tid = threadIdx.x;
     const int cg = (tid & 15) * 4;
     const int rg = tid >> 4;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int il = tc.i0 + rg + 16 * p;
-        const int jl = tc.j0 + cg;
-        // element (il, jl + e) of the canonical frame lives at stored (il, jl + e)
-        // or (jl + e, il); zero whichever is valid
+        // canonical (i, j) lives at stored (j, i): stored row j0 + rl, columns i0 + cg .. +3
+        const int r = tc.j0 + rg + 16 * p;
+        const int c = tc.i0 + cg;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = il, j = jl + e;
-            if (i < d.m && j < d.n) {
-                const int64_t idx = d.transposed ? d.p_off + (int64_t)j * d.C + i : d.p_off + (int64_t)i * d.C + j;
-                mom[idx] = 0.f;
-            }
-        }
+        for (int e = 0; e < 4; ++e)
+            if (r < d.R && c + e < d.C) mom[d.p_off + (int64_t)r * d.C + c + e] = 0.f;
     }
 }
 

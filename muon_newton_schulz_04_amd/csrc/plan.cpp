@@ -216,10 +216,16 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
                 d.a_off = P.a_elems;
                 d.row_off = (int32_t)P.rows_total;
                 d.rowpart_off = nm ? P.rowpart_elems : 0;
-                // elementwise tiles cover the valid block rounded up to 64: the
-                // X~ padding beyond it is zeroed once at init and never written
-                d.ew_tiles_n = (d.n + kEwTile - 1) / kEwTile;
-                d.ew_count = ((d.m + kEwTile - 1) / kEwTile) * d.ew_tiles_n;
+                // elementwise tiles: 64 x 64 over the valid block rounded up to
+                // 64 (transposed), else runs of kEwLinear stored elements; the X~
+                // padding outside them is zeroed once at init and never written
+                if (d.transposed) {
+                    d.ew_tiles_n = (d.n + kEwTile - 1) / kEwTile;
+                    d.ew_count = ((d.m + kEwTile - 1) / kEwTile) * d.ew_tiles_n;
+                } else {
+                    d.ew_tiles_n = 0;
+                    d.ew_count = (int32_t)((t.rows * t.cols + kEwLinear - 1) / kEwLinear);
+                }
                 d.ew_start = (int32_t)ew_tiles;
                 P.x_elems += (int64_t)d.m_pad * d.n_pad;
                 P.a_elems += (int64_t)d.m_pad * d.m_pad;
@@ -310,8 +316,14 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
             for (int ti = 0; ti < tm; ++ti)
                 for (int tj = ti + 1; tj < tm; ++tj) gl.push_back({mi, (int16_t)ti, (int16_t)tj});
             for (int ti = 0; ti < tm; ++ti) gl.push_back({mi, (int16_t)ti, (int16_t)ti});
-            for (int ti = 0; ti < tm; ++ti)
-                for (int tj = 0; tj < tn; ++tj) ul.push_back({mi, (int16_t)ti, (int16_t)tj});
+            // update tiles in column blocks of at most one XCD's CU count, of
+            // near-equal width: the workgroups that run together read every
+            // row panel of B but only W column panels of X, not all of them
+            const int nb = (tn + std::max(1, kCusPerXcd / tm) - 1) / std::max(1, kCusPerXcd / tm);
+            const int W = (tn + nb - 1) / nb;
+            for (int tb = 0; tb < tn; tb += W)
+                for (int ti = 0; ti < tm; ++ti)
+                    for (int tj = tb; tj < std::min(tn, tb + W); ++tj) ul.push_back({mi, (int16_t)ti, (int16_t)tj});
             g.push_back(gl);
             u.push_back(ul);
             cg.push_back(d.n_pad);

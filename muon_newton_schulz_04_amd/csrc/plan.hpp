@@ -22,6 +22,8 @@ namespace muon {
 constexpr int kMaxGroups = 4;
 constexpr int kMinSplit = 2;
 constexpr int64_t kMaxSplitTiles64 = (int64_t)64 * 256 * 16;
+// Compute units per XCD on MI355X (256 CUs in 8 XCDs).
+constexpr int kCusPerXcd = 32;
 
 struct TileList {
     int T = 0;
