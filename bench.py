@@ -92,7 +92,7 @@ def _pmc_args(workload_id: int):
     """Directory suffix, bench.py arguments and time limit (s) of the counter
     runs for a workload (the 1.5B body's inputs take minutes to generate)."""
     if workload_id == 1:
-        return "", "", 120
+        return "", " --no-other-configs", 120
     return f"_c{workload_id}", f" --config {workload_id}", 300
 
 
@@ -338,7 +338,6 @@ def cpu_baseline(seconds: float) -> dict:
 def env_snapshot() -> dict:
     """Versions and hardware of the run (GPU, ROCm, hipcc, torch, host CPU)."""
     import platform
-    import subprocess
 
     import numpy as np
     import torch
@@ -357,10 +356,12 @@ def env_snapshot() -> dict:
             env["rocm"] = f.read().strip()
     except OSError:
         env["rocm"] = None
+    # the compiler that built libmuon, as the build recorded it (no child
+    # process is started here: under a profiler it would inherit a GPU context)
     try:
-        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=30)
-        env["hipcc"] = " | ".join(x.strip() for x in r.stdout.splitlines() if "version" in x.lower())[:200]
-    except Exception:
+        with open(os.path.join(ROOT, "muon_newton_schulz_04_amd", "libmuon.build.txt")) as f:
+            env["hipcc"] = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("hipcc:")), None)
+    except OSError:
         env["hipcc"] = None
     try:
         with open("/proc/cpuinfo") as f:

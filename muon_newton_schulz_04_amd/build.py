@@ -17,6 +17,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmuon.so")
+# compiler version and flags of the last build, next to the library (read by
+# bench.py's environment record, which runs no compiler itself)
+BUILD_INFO = os.path.join(PKG, "libmuon.build.txt")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "plan.cpp", "schedule.cpp", "kernels_elementwise.hip", "kernels_ns.hip",
@@ -63,6 +66,11 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"linking libmuon.so failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
+    if OUT == os.path.join(PKG, "libmuon.so"):
+        r = subprocess.run([cc, "--version"], capture_output=True, text=True)
+        ver = " | ".join(x.strip() for x in r.stdout.splitlines() if "version" in x.lower())
+        with open(BUILD_INFO, "w") as f:
+            f.write(f"hipcc: {ver}\narch: {ARCH}\nflags (.hip): {' '.join(_flags('x.hip'))}\n")
     return OUT
 
 
