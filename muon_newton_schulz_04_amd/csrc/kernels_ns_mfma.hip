@@ -29,15 +29,13 @@
 //  * The fragment reads of sub-step k+1 run under the MFMAs of sub-step k.
 //  * On diagonal Gram / polynomial tiles both operands are the same rows,
 //    which are loaded once.
-//  * The update computes X' = alpha (a X + B X) with B = b A + c A A as the
-//    polynomial kernel rounded it. The a X term needs the output tile's own
-//    rows of X, which pass through LDS as the K slices that cover the tile's
-//    row range: while such a slice is resident, each wave adds a times its
-//    entries to the accumulators of the rows it owns (8-byte LDS reads laid
-//    out like the accumulators), so X is still read once per iteration and
-//    a X is summed in fp32 before the single rounding of X'. The polynomial
-//    kernel's own A tile (for the b A term) streams into LDS during its last
-//    K slice.
+//  * The polynomial computes B = b A + c A A and the update X' = alpha (a X +
+//    B X), each rounded once. Their b A and a X terms need the output tile's
+//    own block of the stage's input (A, or X), which is loaded into LDS in
+//    three parts under the last two K slices and after the main loop (see
+//    dma_own); the epilogue adds it to the fp32 accumulators before the
+//    rounding. The update's epilogue writes X' back over that block in LDS
+//    and stores from there.
 //
 // Source of the iteration: [P4] "modded-nanogpt 50B-token 长时程训练实验解析",
 // section "从源码看 Muon 的分布式正交化实现" (quintic Newton–Schulz in bf16).
