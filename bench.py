@@ -37,12 +37,20 @@ GRAD_POOL = 4               # distinct gradient sets cycled through the timed st
 
 
 def _kernel_source_hash() -> str:
+    """Hash of the kernel and planner sources with comments and blank space
+    removed, so that a committed counter summary stays matched to the code it
+    was taken on across comment-only edits."""
+    import re
     h = hashlib.sha256()
     for f in ("kernels_ns.hip", "kernels_ns_mfma.hip", "kernels_ns_small.hip", "kernels_elementwise.hip",
               "kernel_common.hpp",
               "device_types.hpp", "plan.cpp", "api.cpp"):
-        with open(os.path.join(ROOT, "muon_newton_schulz_04_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "muon_newton_schulz_04_amd", "csrc", f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)   # block comments
+        src = re.sub(r"//[^\n]*", "", src)                  # line comments
+        src = "\n".join(ln.strip() for ln in src.splitlines() if ln.strip())
+        h.update(src.encode("utf-8"))
     return h.hexdigest()[:16]
 
 
