@@ -42,8 +42,8 @@ def _kernel_source_hash() -> str:
     was taken on across comment-only edits."""
     import re
     h = hashlib.sha256()
-    for f in ("kernels_ns.hip", "kernels_ns_mfma.hip", "kernels_ns_small.hip", "kernels_elementwise.hip",
-              "kernel_common.hpp",
+    for f in ("kernels_ns.hip", "kernels_ns_mfma.hip", "kernels_ns_small.hip", "kernels_ns_panel.hip",
+              "kernels_elementwise.hip", "kernel_common.hpp", "ns_mfma_common.hpp",
               "device_types.hpp", "plan.cpp", "api.cpp"):
         with open(os.path.join(ROOT, "muon_newton_schulz_04_amd", "csrc", f), encoding="utf-8") as fh:
             src = fh.read()
@@ -205,13 +205,13 @@ def mfma_summary(pmc_dir: str, workload_id: int) -> dict:
 
 
 def _kernel_class(name: str) -> str:
-    """gram / poly / update / ns_small / momentum / apply / copy for a kernel name, or '' otherwise."""
+    """gram / poly / update / ns_small / ns_panel / momentum / apply / copy for a kernel name, or '' otherwise."""
     if "neg_kernel" in name:
         return "copy"
     if "k_ns_big<" in name or "k_ns<" in name:
         mode = name.split("<", 1)[1].split(">", 1)[0].split(",")
         return {"0": "gram", "1": "poly", "2": "update"}[mode[-2].strip() if "big" in name else mode[2].strip()]
-    for k in ("ns_small", "momentum", "apply"):
+    for k in ("ns_small", "ns_panel", "momentum", "apply"):
         if "k_" + k in name:
             return k
     return ""
@@ -228,7 +228,7 @@ def _short_kernel(name: str) -> str:
     m = re.search(r"k_ns<([^,]+), (\d+), (\d)>", name)
     if m:
         return f"k_ns<{'bf16' if 'bf' in m.group(1) else 'f32'}> {mode[m.group(3)]} T={m.group(2)}"
-    for k in ("k_ns_small", "k_momentum", "k_apply", "k_normuon", "k_zero_momentum", "k_fill_zero"):
+    for k in ("k_ns_small", "k_ns_panel", "k_momentum", "k_apply", "k_normuon", "k_zero_momentum", "k_fill_zero"):
         if k in name:
             return k
     return name[:60]
@@ -467,7 +467,8 @@ def measure(w, steps: int, warmup: int, kernel_steps: int, pool: int, stream_gro
                 entry["pct_hbm_peak"] = entry["gbs"] / PEAK_HBM_GBS * 100
             kernels[name] = entry
         B.muon_profile_read(H1.h, 0, 1)
-        ns_ms = sum(kernels.get(k, {}).get("ms_per_step", 0.0) for k in ("gram", "poly", "update", "ns_small"))
+        ns_ms = sum(kernels.get(k, {}).get("ms_per_step", 0.0)
+                    for k in ("gram", "poly", "update", "ns_small", "ns_panel"))
         res["ns_tflops_kernels"] = ns_flops / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None
         res["kernel_pass_steps"] = kernel_steps
         if kernels:

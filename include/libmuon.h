@@ -223,7 +223,8 @@ enum {
     MUON_VIEW_F = 5,       /* float32 per canonical row: NorMuon row factor */
     MUON_VIEW_STATUS = 6,  /* int32 [num_matrices]: bit 0 = non-finite u seen this step */
     MUON_VIEW_GRAM = 7,    /* the last iteration's A = X X^T: m_pad x m_pad per matrix at its gram_offset
-                              (tiled matrices; the one-workgroup path keeps A in LDS, its region is unspecified) */
+                              (tiled and one-panel matrices; the short-side <= 64 path keeps A in LDS, its
+                              region is unspecified) */
     MUON_VIEW_POLY = 8     /* the last iteration's B = b A + c A A, same layout as MUON_VIEW_GRAM */
 };
 
@@ -264,7 +265,10 @@ enum {
     MUON_KERNEL_APPLY = 5,    /* parameter update */
     MUON_KERNEL_NS_SMALL = 6, /* every Newton-Schulz iteration of the bf16 matrices whose
                                * short side is at most 64 (one workgroup per matrix) */
-    MUON_KERNEL_COUNT = 7
+    MUON_KERNEL_NS_PANEL = 7, /* every Newton-Schulz iteration of the bf16 matrices whose
+                               * short side is 256 and long side at most 4096 (one
+                               * workgroup per matrix, A and B kept in LDS) */
+    MUON_KERNEL_COUNT = 8
 };
 
 /* Algorithmic work of one muon_step for this plan (frozen matrices excluded).

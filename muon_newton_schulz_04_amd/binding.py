@@ -49,8 +49,9 @@ MUON_KERNEL_UPDATE = 3
 MUON_KERNEL_NORMUON = 4
 MUON_KERNEL_APPLY = 5
 MUON_KERNEL_NS_SMALL = 6
-MUON_KERNEL_COUNT = 7
-KERNEL_NAMES = ["momentum", "gram", "poly", "update", "normuon", "apply", "ns_small"]
+MUON_KERNEL_NS_PANEL = 7
+MUON_KERNEL_COUNT = 8
+KERNEL_NAMES = ["momentum", "gram", "poly", "update", "normuon", "apply", "ns_small", "ns_panel"]
 
 
 class muon_matrix(ctypes.Structure):

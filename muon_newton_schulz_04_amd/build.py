@@ -23,7 +23,7 @@ BUILD_INFO = os.path.join(PKG, "libmuon.build.txt")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "plan.cpp", "schedule.cpp", "kernels_elementwise.hip", "kernels_ns.hip",
-           "kernels_ns_mfma.hip", "kernels_ns_small.hip", "static_scratch.hip"]
+           "kernels_ns_mfma.hip", "kernels_ns_small.hip", "kernels_ns_panel.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 
 

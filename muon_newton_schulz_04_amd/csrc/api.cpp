@@ -272,6 +272,7 @@ static muon_status init_impl(muon_handle** out, const muon_matrix* table, int32_
     if (e == hipSuccess) e = up(P.off_ewmap, P.ew_map.data(), P.ew_map.size() * 4);
     if (e == hipSuccess) e = up(P.off_active, P.active.data(), P.active.size() * 4);
     if (e == hipSuccess) e = up(P.off_small, P.small.data(), P.small.size() * 4);
+    if (e == hipSuccess) e = up(P.off_panel, P.panel.data(), P.panel.size() * 4);
     for (const auto& L : P.lists) {
         if (e == hipSuccess) e = up(L.off_gram, L.gram.data(), L.gram.size() * sizeof(muon::TileWork));
         if (e == hipSuccess) e = up(L.off_poly, L.poly.data(), L.poly.size() * sizeof(muon::TileWork));
@@ -401,6 +402,10 @@ static muon_status step_impl(muon_handle* h, float* params, const float* grads, 
         });
         if (s != MUON_OK) return s;
     }
+    muon::NsCoeffs co_all{};
+    std::memcpy(co_all.c, P.hp.ns_coeffs, sizeof(co_all.c));
+    co_all.steps = steps;
+    co_all.eps = P.hp.ns_eps;
     for (int k = 0; k < steps; ++k) {
         void* xin = k == 0 ? L.xt : ((k & 1) ? L.x1 : L.x0);
         void* xout = k == 0 ? L.x1 : ((k & 1) ? L.x0 : L.x1);
@@ -408,6 +413,14 @@ static muon_status step_impl(muon_handle* h, float* params, const float* grads, 
         const int first = k == 0;
         const int rowstats = (k == steps - 1) && P.hp.normuon;
         for (int grp = 0; grp < P.n_groups; ++grp) {
+            // the group's one-panel matrices: every iteration in one launch
+            const int np = P.panel_begin[grp + 1] - P.panel_begin[grp];
+            if (k == 0 && np > 0) {
+                const int32_t* pl = reinterpret_cast<const int32_t*>(h->ws + P.off_panel) + P.panel_begin[grp];
+                s = run_on(sg[grp], MUON_KERNEL_NS_PANEL, "panel Newton-Schulz kernel",
+                           [&] { return muon::launch_ns_panel(Lg[grp], pl, np, co_all, P.hp.normuon); });
+                if (s != MUON_OK) return s;
+            }
             for (const auto& T : P.lists) {
                 if (T.group != grp) continue;
                 const muon::GemmList G = make_list(h, T);
@@ -546,6 +559,8 @@ muon_status muon_work_stats(const muon_handle* h, muon_work* out) {
         const double f_gram = steps * m * (m + 1) * n, f_poly = steps * m * (m + 1) * m, f_upd = steps * 2.0 * m * m * n;
         if (P.is_small(d)) {
             out->flops[MUON_KERNEL_NS_SMALL] += f_gram + f_poly + f_upd;
+        } else if (P.is_panel(d)) {
+            out->flops[MUON_KERNEL_NS_PANEL] += f_gram + f_poly + f_upd;
         } else {
             out->flops[MUON_KERNEL_GRAM] += f_gram;
             out->flops[MUON_KERNEL_POLY] += f_poly;
@@ -566,6 +581,8 @@ muon_status muon_work_stats(const muon_handle* h, muon_work* out) {
     out->launches[MUON_KERNEL_POLY] = steps * nl;
     out->launches[MUON_KERNEL_UPDATE] = steps * nl;
     out->launches[MUON_KERNEL_NS_SMALL] = P.small.empty() ? 0 : 1;
+    for (int g = 0; g < P.n_groups; ++g)
+        out->launches[MUON_KERNEL_NS_PANEL] += P.panel_begin[g + 1] > P.panel_begin[g] ? 1 : 0;
     out->launches[MUON_KERNEL_NORMUON] = P.hp.normuon ? any * P.n_groups : 0;
     out->launches[MUON_KERNEL_APPLY] = any * P.n_groups;
     return MUON_OK;

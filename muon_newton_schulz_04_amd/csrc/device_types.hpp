@@ -19,6 +19,11 @@ constexpr int kThreads = 256;
 // bf16 matrices with m_pad = 64 and n_pad <= kSmallMaxNPad run every
 // Newton–Schulz iteration in one workgroup (X, A, P resident in LDS).
 constexpr int kSmallMaxNPad = 512;
+// bf16 matrices that are one 256-row panel (m_pad = 256 on 256-tiles) with
+// n_pad <= kPanelMaxNPad run every iteration in one workgroup of 8 waves
+// (A and B resident in LDS).
+constexpr int kPanelRows = 256;
+constexpr int kPanelMaxNPad = 4096;
 
 // One (sub-)matrix of the table, in both frames.
 //   stored frame:    [R, C] row-major at p_off in params / grads / momentum

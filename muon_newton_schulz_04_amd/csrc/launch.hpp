@@ -76,6 +76,13 @@ hipError_t launch_ns_stage_big(const LaunchCtx& L, const GemmList& G, int mode, 
 // (m_pad = 64, n_pad <= n_pad_max <= 512), one workgroup per matrix, reading
 // X~ and writing the output to `out` (same padded canonical layout); with
 // rowstats, also the NorMuon row partial sums.
+// Every iteration of the bf16 Newton–Schulz for the one-panel matrices in
+// `list` (m_pad = 256 on 256-tiles, n_pad <= kPanelMaxNPad), one workgroup per
+// matrix, with the iterations' X ping-pong in xt -> x1 -> x0 -> x1 ... (the
+// tiled path's buffers), the last iteration's A and B in the workspace and,
+// with rowstats, the NorMuon row partial sums.
+hipError_t launch_ns_panel(const LaunchCtx& L, const int32_t* list, int n, const NsCoeffs& co, int rowstats);
+
 hipError_t launch_ns_small(const LaunchCtx& L, const int32_t* list, int n, int n_pad_max, const NsCoeffs& co,
                            void* out, int rowstats);
 size_t ns_small_lds_bytes(int n_pad_max);

@@ -293,6 +293,14 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
         while (g <= P.n_groups) P.ew_begin[g++] = (int)P.ew_map.size();
     }
 
+    // ---- one-panel matrices, group by group ----
+    for (int grp = 0; grp < P.n_groups; ++grp) {
+        P.panel_begin[grp] = (int)P.panel.size();
+        for (int k = P.act_begin[grp]; k < P.act_begin[grp + 1]; ++k)
+            if (P.is_panel(P.mats[P.active[k]])) P.panel.push_back(P.active[k]);
+    }
+    P.panel_begin[P.n_groups] = (int)P.panel.size();
+
     // ---- GEMM work lists per (group, tile size) ----
     for (int grp = 0; grp < P.n_groups; ++grp)
     for (int T : {256, 128, 64}) {
@@ -308,7 +316,7 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
                 }
                 continue;
             }
-            if (group_of[mi] != grp) continue;
+            if (group_of[mi] != grp || P.is_panel(d)) continue;
             const int tm = d.m_pad / T, tn = d.n_pad / T;
             std::vector<TileWork> gl, ul;
             // the matrix's upper tiles, the diagonal ones last: they compute
@@ -364,6 +372,7 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
     P.off_ewmap = take(P.ew_map.size() * 4);
     P.off_active = take(P.active.size() * 4);
     P.off_small = take(P.small.size() * 4);
+    P.off_panel = take(P.panel.size() * 4);
     for (auto& L : P.lists) {
         L.off_gram = take(L.gram.size() * sizeof(TileWork));
         L.off_poly = take(L.poly.size() * sizeof(TileWork));

@@ -49,6 +49,9 @@ struct Plan {
     // act_begin[g] .. act_begin[g+1]) and tiles [ew_begin[g], ew_begin[g+1])
     int act_begin[kMaxGroups + 1] = {};
     int ew_begin[kMaxGroups + 1] = {};
+    std::vector<int32_t> panel;         // one-panel matrices, group by group
+    int panel_begin[kMaxGroups + 1] = {};
+    size_t off_panel = 0;
     std::vector<int32_t> small;         // active matrices of the one-workgroup Newton–Schulz
     int small_np = 0;                   // their largest n_pad
     size_t off_small = 0;
@@ -63,6 +66,9 @@ struct Plan {
     // 64-bit sums used by tools and tests
     double ns_alg_flops = 0.0;          // per step, symmetric products counted as m(m+1)k
     bool is_small(const MatDesc& d) const { return esize == 2 && d.T == 64 && d.n_pad <= kSmallMaxNPad; }
+    bool is_panel(const MatDesc& d) const {
+        return esize == 2 && d.T == kPanelRows && d.m_pad == kPanelRows && d.n_pad <= kPanelMaxNPad;
+    }
 };
 
 // Validate and build. Returns MUON_OK or an error code with *err set.

@@ -20,6 +20,7 @@ hipError_t launch_ns_stage_big(const LaunchCtx&, const GemmList&, int, const voi
                                float, int, float, int) {
     return hipErrorNotSupported;
 }
+hipError_t launch_ns_panel(const LaunchCtx&, const int32_t*, int, const NsCoeffs&, int) { return hipSuccess; }
 hipError_t launch_ns_small(const LaunchCtx&, const int32_t*, int, int, const NsCoeffs&, void*, int) {
     return hipErrorNotSupported;
 }

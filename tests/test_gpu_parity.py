@@ -86,6 +86,27 @@ def test_ragged_bf16_all_stages(normuon):
     _run_all_stages(w, 3)
 
 
+# matrices that are one 256-row panel (every iteration in one workgroup,
+# A and B in LDS), next to one just beyond the panel kernel's limit
+PANEL = [
+    (256, 256, 2, "spike"),               # a single 256-column block
+    (256, 990, 1, "spike"),               # n_pad 1024, Gram K trimmed to 992
+    (990, 256, 1, "spike"),               # tall -> transposed
+    (256, 4096, 1, "spike"),              # the largest panel: 16 column blocks
+    (256, 4100, 1, "spike"),              # n_pad 4352: the tiled kernels
+    (256, 768, 1, "rank8"),
+    (256, 512, 1, "zero"),
+    (256, 300, 1, "student_t", 0.0),      # lr_mul 0
+    (300, 256, 1, "gauss", 1.0, 1),       # frozen
+]
+
+
+@pytest.mark.parametrize("normuon", [0, 1])
+def test_panel_matrices_all_stages(normuon):
+    w = custom_workload(150 + normuon, PANEL, steps=3, normuon=normuon, lr=0.05, weight_decay=0.05 * normuon)
+    _run_all_stages(w, 3)
+
+
 # every matrix on 128 / 256 tiles, decoupled weight decay with per-matrix
 # lr_mul / wd_mul, ragged edges, transposed blocks, zero and frozen matrices
 LARGE_TILES = [
@@ -135,7 +156,8 @@ def _run_with_coeffs(w, steps, coeffs, sharp, **hp):
         assert_worst(worst, fp32=run.fp32)
 
 
-STEP_SHAPES = [(400, 520, 1, "spike"), (200, 300, 1, "spike"), (48, 1000, 1, "gauss"), (64, 64, 2, "gauss")]
+STEP_SHAPES = [(400, 520, 1, "spike"), (200, 300, 1, "spike"), (48, 1000, 1, "gauss"), (64, 64, 2, "gauss"),
+               (256, 640, 1, "spike")]
 
 
 @pytest.mark.parametrize("ns_steps", [1, 10, 16])
@@ -164,7 +186,8 @@ def test_newton_schulz_step_counts_convergent_tail(ns_steps):
 def test_stream_groups_give_identical_results():
     # the 9 tiled matrices split over 2, 3 or 4 streams, or all on the
     # caller's stream: the same kernels on the same tiles, so bit-identical
-    w = custom_workload(110, LARGE_TILES + [(200, 300, 2, "spike"), (64, 64, 3, "rank8")], steps=2, lr=0.05,
+    w = custom_workload(110, LARGE_TILES + [(200, 300, 2, "spike"), (64, 64, 3, "rank8"), (256, 512, 2, "spike")],
+                        steps=2, lr=0.05,
                         weight_decay=0.1, normuon=1)
     runs = [GpuRun(w, stream_groups=g) for g in (1, 2, 3, 4)]
     for t in range(2):
