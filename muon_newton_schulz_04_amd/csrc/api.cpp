@@ -359,9 +359,10 @@ static muon_status step_impl(muon_handle* h, float* params, const float* grads, 
         return MUON_OK;
     };
     const int steps = P.hp.ns_steps;
-    // Each stream group runs its whole chain: momentum of its matrices (and,
-    // in group 0, the small-matrix Newton–Schulz), its tiled Newton–Schulz
-    // launches, NorMuon and the parameter update. Group 0 runs on the
+    // Each stream group runs its whole chain: momentum of its matrices, its
+    // one-panel Newton–Schulz launch (all iterations; in group 0 followed by
+    // the small-matrix one), its tiled Newton–Schulz launches, NorMuon and the
+    // parameter update. Group 0 runs on the
     // caller's stream; group g > 0 on the handle's stream g - 1, which starts
     // once group g - 1's momentum is done and joins the caller's stream at
     // the end. The stagger puts each group's momentum under the previous
@@ -391,17 +392,6 @@ static muon_status step_impl(muon_handle* h, float* params, const float* grads, 
             if (e != hipSuccess) return hip_fail(h, e, "stream fork");
         }
     }
-    if (!P.small.empty()) {
-        muon::NsCoeffs co{};
-        std::memcpy(co.c, P.hp.ns_coeffs, sizeof(co.c));
-        co.steps = steps;
-        co.eps = P.hp.ns_eps;
-        s = run_on(sg[0], MUON_KERNEL_NS_SMALL, "small-matrix Newton-Schulz kernel", [&] {
-            return muon::launch_ns_small(Lg[0], reinterpret_cast<const int32_t*>(h->ws + P.off_small),
-                                         (int)P.small.size(), P.small_np, co, ns_out(h), P.hp.normuon);
-        });
-        if (s != MUON_OK) return s;
-    }
     muon::NsCoeffs co_all{};
     std::memcpy(co_all.c, P.hp.ns_coeffs, sizeof(co_all.c));
     co_all.steps = steps;
@@ -419,6 +409,15 @@ static muon_status step_impl(muon_handle* h, float* params, const float* grads, 
                 const int32_t* pl = reinterpret_cast<const int32_t*>(h->ws + P.off_panel) + P.panel_begin[grp];
                 s = run_on(sg[grp], MUON_KERNEL_NS_PANEL, "panel Newton-Schulz kernel",
                            [&] { return muon::launch_ns_panel(Lg[grp], pl, np, co_all, P.hp.normuon); });
+                if (s != MUON_OK) return s;
+            }
+            // the small matrices, after group 0's panel workgroups (which hold a
+            // whole CU each for all iterations) so that they fill the other CUs
+            if (k == 0 && grp == 0 && !P.small.empty()) {
+                s = run_on(sg[0], MUON_KERNEL_NS_SMALL, "small-matrix Newton-Schulz kernel", [&] {
+                    return muon::launch_ns_small(Lg[0], reinterpret_cast<const int32_t*>(h->ws + P.off_small),
+                                                 (int)P.small.size(), P.small_np, co_all, ns_out(h), P.hp.normuon);
+                });
                 if (s != MUON_OK) return s;
             }
             for (const auto& T : P.lists) {
