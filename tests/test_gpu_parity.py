@@ -513,6 +513,33 @@ def test_checkpoint_resume_is_bit_identical():
     assert torch.any(ref.H.view(B.MUON_VIEW_V, torch.float32) != 0)
 
 
+def test_work_split_between_panel_small_and_tiled_kernels():
+    # which kernel runs which matrix: 256-row panels up to n_pad 4096 in the
+    # panel kernel (one launch per stream group that has any), 64-row
+    # matrices with n_pad <= 512 in the small kernel, the rest tiled; the
+    # algorithmic flops follow the matrices
+    shapes = [(256, 1024, 3, "spike"), (2048, 256, 1, "spike"), (256, 4100, 1, "spike"), (64, 300, 2, "gauss"),
+              (768, 768, 2, "spike"), (256, 512, 1, "gauss", 1.0, 1)]
+    w = custom_workload(160, shapes, steps=1)
+
+    def flops(m, n, steps=5):
+        return steps * (m * (m + 1) * n + m * (m + 1) * m + 2 * m * m * n)
+
+    for groups in (1, 3):
+        H = B.MuonHandle(w.entries, B.make_hparams(stream_groups=groups))
+        ws = B.muon_work_stats(H.h)
+        panel = 3 * flops(256, 1024) + flops(256, 2048)
+        small = 2 * flops(64, 300)
+        tiled = flops(256, 4100) + 2 * flops(768, 768)
+        assert ws.flops[B.MUON_KERNEL_NS_PANEL] == pytest.approx(panel, rel=1e-12)
+        assert ws.flops[B.MUON_KERNEL_NS_SMALL] == pytest.approx(small, rel=1e-12)
+        tiled_sum = sum(ws.flops[k] for k in (B.MUON_KERNEL_GRAM, B.MUON_KERNEL_POLY, B.MUON_KERNEL_UPDATE))
+        assert tiled_sum == pytest.approx(tiled, rel=1e-12)
+        assert ws.launches[B.MUON_KERNEL_NS_SMALL] == 1
+        assert 1 <= ws.launches[B.MUON_KERNEL_NS_PANEL] <= groups
+        del H
+
+
 def test_empty_and_all_frozen_tables_are_noops():
     w = custom_workload(107, [(64, 64, 2, "gauss", 1.0, 1)], steps=1)
     run = GpuRun(w)
