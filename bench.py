@@ -431,7 +431,7 @@ def measure(w, steps: int, warmup: int, kernel_steps: int, pool: int, stream_gro
     per_step = [ev[t].elapsed_time(ev[t + 1]) for t in range(steps)]
     ms = ev[0].elapsed_time(ev[steps]) / steps
     ns_flops = sum(work.flops[k] for k in (B.MUON_KERNEL_GRAM, B.MUON_KERNEL_POLY, B.MUON_KERNEL_UPDATE,
-                                            B.MUON_KERNEL_NS_SMALL))
+                                            B.MUON_KERNEL_NS_SMALL, B.MUON_KERNEL_NS_PANEL))
     fp32 = w.ns_precision == "fp32"
     peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
     res = {"workload": w.name, "steps": steps, "warmup": warmup, "grad_sets": pool, "ms_per_step": ms,
