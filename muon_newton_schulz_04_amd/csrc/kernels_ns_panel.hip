@@ -6,19 +6,19 @@
 // most of each launch in prologues and epilogues. Here the workgroup keeps A
 // and then B resident in LDS (128 KB, bf16) across the three stages of an
 // iteration:
-//  * Gram: X streams through a ring of 32-wide K slices (direct-to-LDS
-//    loads into the resident region, which is idle until the epilogue);
-//    the waves compute the blocks on or above the diagonal, and the epilogue
+//  * Gram: X streams through four 64-wide K slices (direct-to-LDS loads into
+//    the resident region, which is idle until the epilogue); the waves
+//    compute the 32 x 32 blocks on or above the diagonal, and the epilogue
 //    writes A = R(g X X^T) and its mirror into the resident region.
 //  * Polynomial: A A from the resident A (no global loads), all 64 blocks;
 //    the epilogue reads each lane's own A entries and writes
 //    B = R(b A + c A A) over them.
-//  * Update: for each 256-column block of X, the block streams through a
-//    second ring (32-row slices) while B is read from LDS; a X is added to
-//    the accumulators from the slice that holds the output rows' own X (all
-//    waves run the same code, with a = 0 where the rows are not theirs), and
-//    X' = R(h (a X + B X)) is stored to global memory, where the next
-//    iteration's Gram reads it.
+//  * Update: for each 256-column block of X, the block streams through two
+//    32-row slice buffers after the resident region while B is read from
+//    LDS; the waves that own a slice's rows add a X from it to their
+//    accumulators, and X' = R(h (a X + B X)) leaves through the idle slice
+//    buffers in 64-row rounds as full-line stores, for the next iteration's
+//    Gram to read.
 // g = s^2 and h = s in iteration 0 (s from the momentum kernel's partial
 // sums), 1 afterwards; the rounding points are those of the tiled kernels.
 // The last iteration also writes A and B to the workspace (debug views) and,
@@ -77,10 +77,8 @@ __device__ __forceinline__ int opaque(int x) {
 // chunk c ^ (r & 15), so the 16 rows of a ds_read_b128 phase fall in 16
 // distinct 16-byte bank slots.
 __device__ __forceinline__ int res_off(int r, int chunk) { return r * RROW + 16 * (chunk ^ (r & 15)); }
-// the 8 bytes of row r, columns c .. c+3 (c % 4 == 0)
-__device__ __forceinline__ int res_off8(int r, int c) { return res_off(r, c >> 3) + 2 * (c & 7); }
-// one bf16 of row r, column c
-__device__ __forceinline__ int res_off2(int r, int c) { return res_off(r, c >> 3) + 2 * (c & 7); }
+// the bf16 of row r, column c (with c % 4 == 0 also the 8 bytes of columns c .. c+3)
+__device__ __forceinline__ int res_elem(int r, int c) { return res_off(r, c >> 3) + 2 * (c & 7); }
 
 template <bool ROWSTATS>
 __global__ __launch_bounds__(PNT) void k_ns_panel(const MatDesc* __restrict__ mats, const int32_t* __restrict__ list,
@@ -287,12 +285,12 @@ __global__ __launch_bounds__(PNT) void k_ns_panel(const MatDesc* __restrict__ ma
                         uint2 w;
                         w.x = pack_bf16x2(v0, v1);
                         w.y = pack_bf16x2(v2, v3);
-                        *reinterpret_cast<uint2*>(smem + res_off8(i, j)) = w;
+                        *reinterpret_cast<uint2*>(smem + res_elem(i, j)) = w;
                         if (mirror) {
-                            *reinterpret_cast<uint16_t*>(smem + res_off2(j + 0, i)) = (uint16_t)(w.x & 0xffffu);
-                            *reinterpret_cast<uint16_t*>(smem + res_off2(j + 1, i)) = (uint16_t)(w.x >> 16);
-                            *reinterpret_cast<uint16_t*>(smem + res_off2(j + 2, i)) = (uint16_t)(w.y & 0xffffu);
-                            *reinterpret_cast<uint16_t*>(smem + res_off2(j + 3, i)) = (uint16_t)(w.y >> 16);
+                            *reinterpret_cast<uint16_t*>(smem + res_elem(j + 0, i)) = (uint16_t)(w.x & 0xffffu);
+                            *reinterpret_cast<uint16_t*>(smem + res_elem(j + 1, i)) = (uint16_t)(w.x >> 16);
+                            *reinterpret_cast<uint16_t*>(smem + res_elem(j + 2, i)) = (uint16_t)(w.y & 0xffffu);
+                            *reinterpret_cast<uint16_t*>(smem + res_elem(j + 3, i)) = (uint16_t)(w.y >> 16);
                         }
                     }
                 }
@@ -329,7 +327,7 @@ __global__ __launch_bounds__(PNT) void k_ns_panel(const MatDesc* __restrict__ ma
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
                         const int j = 32 * colblk(fj) + 8 * gq + 4 * opaque(hi);
-                        uint2* pv = reinterpret_cast<uint2*>(smem + res_off8(i, j));
+                        uint2* pv = reinterpret_cast<uint2*>(smem + res_elem(i, j));
                         const uint2 av = *pv;
                         const float v0 = fmaf(cb, bf16_lo(av.x), cc * acc[fi][fj][4 * gq + 0]);
                         const float v1 = fmaf(cb, bf16_hi(av.x), cc * acc[fi][fj][4 * gq + 1]);
@@ -413,7 +411,7 @@ __global__ __launch_bounds__(PNT) void k_ns_panel(const MatDesc* __restrict__ ma
                                 uint2 w;
                                 w.x = pack_bf16x2(av[4 * gq + 0] * h, av[4 * gq + 1] * h);
                                 w.y = pack_bf16x2(av[4 * gq + 2] * h, av[4 * gq + 3] * h);
-                                *reinterpret_cast<uint2*>(smem + RING + res_off8(rl, j)) = w;
+                                *reinterpret_cast<uint2*>(smem + RING + res_elem(rl, j)) = w;
                                 if (ROWSTATS && last) {
                                     const float r0 = bf16_lo(w.x), r1 = bf16_hi(w.x), r2 = bf16_lo(w.y),
                                                 r3 = bf16_hi(w.y);
