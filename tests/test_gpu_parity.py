@@ -282,6 +282,26 @@ def test_ragged_fp32_all_stages():
     _run_all_stages(w, 3)
 
 
+def test_fp32_group_larger_than_the_mall():
+    # one stream group writing 285 MB of X~ (more than the 256 MB MALL): the
+    # momentum kernel stores X~ nontemporally, in the runs of the untransposed
+    # matrices and in the transposed matrices' tiles; one matrix of each
+    # orientation is checked against the oracle
+    w = custom_workload(118, [(2048, 4352, 4, "spike"), (4352, 2048, 4, "gauss")], steps=2,
+                        ns_precision="fp32", lr=0.05)
+    _say(f"[case] {w.name}: {w.num_matrices} matrices, {w.total} elements, one stream group")
+    run = GpuRun(w, stream_groups=1)
+    sample = [1, 6]
+    orc_m = {gi: np.zeros((run.subs[gi][4], run.subs[gi][5])) for gi in sample}
+    for t in range(w.steps):
+        p_prev, v_prev = snapshot(run, sample)
+        g = run.load_grads(t)
+        run.step()
+        worst = check_stages(run, t, sample, grads_host=g, p_prev=p_prev, v_prev=v_prev, orc_m=orc_m)
+        _say(f"  step {t}: {worst}")
+        assert_worst(worst, fp32=True)
+
+
 def test_heavy_ball_and_weight_decay_and_steps():
     # heavy-ball momentum, Nesterov off, decoupled weight decay, 7 NS steps with
     # a per-iteration coefficient schedule whose last step is the cubic
