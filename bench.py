@@ -550,8 +550,8 @@ def main() -> int:
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the sharded "
-              "multi-GPU step is not part of it.", file=sys.stderr)
+        print(f"bench.py: libmuon's step runs on one GPU only (asked for --gpus {args.gpus}); a sharded "
+              "multi-GPU step is not implemented.", file=sys.stderr)
         return 2
 
     import torch

@@ -18,7 +18,7 @@ Sources (cited by page title and section):
        statistic taken along the longer dimension with rsqrt scaling per lane;
        section "改动一" (change 1): per-matrix lr_mul / wd_mul.
 
-Readings where the pages are silent or garbled (each listed in the design doc):
+Readings where the pages are silent or garbled:
   R1 lerp momentum m <- beta*m + (1-beta)*g (P2) as the default; the heavy-ball
      form of P4 is kept as an option. Both give the same NS input up to a
      positive scale, which the normalisation removes.

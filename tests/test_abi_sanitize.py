@@ -6,7 +6,7 @@ api.cpp, plan.cpp and schedule.cpp are compiled with g++ and
 (tests/native/launch_stubs.cpp) and the HIP runtime, and driven by
 tests/native/abi_check.c: table validation, planning of the five workloads'
 tables, argument checks of every entry point and the host schedules. Any
-sanitizer report aborts the driver.
+sanitizer report aborts the check program.
 """
 
 import os
