@@ -389,47 +389,43 @@ __global__ __launch_bounds__(PNT) void k_ns_panel(const MatDesc* __restrict__ ma
                         }
                 }
             });
-            // X' leaves through the idle ring in four rounds of 64 rows: the
-            // waves that own the rows write them as bf16 (512-byte rows, chunk
-            // c at c ^ (r & 15)), then every thread stores whole 16-byte chunks,
-            // so each store instruction covers full cache lines
+            // X' leaves through the idle ring in four rounds of 64 rows:
+            // round R takes row block R of both wave rows (rows 32 R .. +31 and
+            // 128 + 32 R .. +31), so all eight waves write their share as bf16
+            // (512-byte rows, chunk c at c ^ (r & 15)); then every thread
+            // stores whole 16-byte chunks, so each store instruction covers
+            // full cache lines
             bf16* obase = xout + d.x_off + jb * PT;
             __syncthreads();  // every wave is done with the ring's last slice
-            static_for<0, 4>([&](auto r_c) {
+            static_for<0, PFRI>([&](auto r_c) {
                 constexpr int R = decltype(r_c)::value;
-                if (wi == R / 2) {
+                const int rl = wi * 32 + opaque(l32);  // row within the round
 #pragma unroll
-                    for (int fl = 0; fl < 2; ++fl) {
-                        constexpr int FB = 2 * (R % 2);
-                        const int rl = fl * 32 + opaque(l32);  // row within the round
+                for (int fj = 0; fj < PFRJ; ++fj)
 #pragma unroll
-                        for (int fj = 0; fj < PFRJ; ++fj)
-#pragma unroll
-                            for (int gq = 0; gq < 4; ++gq) {
-                                const int j = 32 * colblk(fj) + 8 * gq + 4 * hi;
-                                const f32x16& av = acc[FB + fl][fj];
-                                uint2 w;
-                                w.x = pack_bf16x2(av[4 * gq + 0] * h, av[4 * gq + 1] * h);
-                                w.y = pack_bf16x2(av[4 * gq + 2] * h, av[4 * gq + 3] * h);
-                                *reinterpret_cast<uint2*>(smem + RING + res_elem(rl, j)) = w;
-                                if (ROWSTATS && last) {
-                                    const float r0 = bf16_lo(w.x), r1 = bf16_hi(w.x), r2 = bf16_lo(w.y),
-                                                r3 = bf16_hi(w.y);
-                                    rsq[FB + fl] = fmaf(r0, r0, rsq[FB + fl]);
-                                    rsq[FB + fl] = fmaf(r1, r1, rsq[FB + fl]);
-                                    rsq[FB + fl] = fmaf(r2, r2, rsq[FB + fl]);
-                                    rsq[FB + fl] = fmaf(r3, r3, rsq[FB + fl]);
-                                }
-                            }
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int j = 32 * colblk(fj) + 8 * gq + 4 * hi;
+                        const f32x16& av = acc[R][fj];
+                        uint2 w;
+                        w.x = pack_bf16x2(av[4 * gq + 0] * h, av[4 * gq + 1] * h);
+                        w.y = pack_bf16x2(av[4 * gq + 2] * h, av[4 * gq + 3] * h);
+                        *reinterpret_cast<uint2*>(smem + RING + res_elem(rl, j)) = w;
+                        if (ROWSTATS && last) {
+                            const float r0 = bf16_lo(w.x), r1 = bf16_hi(w.x), r2 = bf16_lo(w.y), r3 = bf16_hi(w.y);
+                            rsq[R] = fmaf(r0, r0, rsq[R]);
+                            rsq[R] = fmaf(r1, r1, rsq[R]);
+                            rsq[R] = fmaf(r2, r2, rsq[R]);
+                            rsq[R] = fmaf(r3, r3, rsq[R]);
+                        }
                     }
-                }
                 __syncthreads();
 #pragma unroll
                 for (int q = 0; q < 64 * (PT / 8) / PNT; ++q) {
                     const int id = opaque(tid) + PNT * q;
-                    const int rr = id >> 5, c = id & 31;
+                    const int rr = id >> 5, c = id & 31;  // staged row rr: wave row rr / 32, row rr % 32 of block R
                     const u32x4 v = *reinterpret_cast<const u32x4*>(smem + RING + res_off(rr, c));
-                    *reinterpret_cast<u32x4*>(obase + (int64_t)(64 * R + rr) * ldx + 8 * c) = v;
+                    const int grow = (rr >> 5) * PWTM + 32 * R + (rr & 31);
+                    *reinterpret_cast<u32x4*>(obase + (int64_t)grow * ldx + 8 * c) = v;
                 }
                 __syncthreads();  // the staged rows are stored before the next round
             });
