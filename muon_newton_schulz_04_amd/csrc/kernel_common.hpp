@@ -13,11 +13,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// float -> bf16, round to nearest even (lowers to v_cvt_pk_bf16_f32).
+// Two floats rounded to bf16 (nearest even) and packed, lo in bits 0..15: one
+// two-wide conversion, which gfx950 does in one v_cvt_pk_bf16_f32.
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+typedef bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    bf16 a = (bf16)lo;
-    bf16 b = (bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2_cvt f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_cvt));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
