@@ -471,34 +471,46 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         // X' = alpha (a X + B X), in place: each lane reads its own 8-byte
         // groups X[il][jl .. jl+3] from the own tile and writes the rounded
         // result back to the same bytes (no other lane touches them); the
-        // tile then leaves from this layout
+        // tile then leaves from this layout. alpha is 1 after the first
+        // iteration, where the multiply is left out (exact either way).
+        auto own_update = [&](auto scaled) __attribute__((always_inline)) {
 #pragma unroll
-        for (int fi = 0; fi < FRI; ++fi) {
-            char* row = own_row(wi * WTM + fi * 32 + l32) + 8 * hi;
+            for (int fi = 0; fi < FRI; ++fi) {
+                char* row = own_row(wi * WTM + fi * 32 + l32) + 8 * hi;
 #pragma unroll
-            for (int fj = 0; fj < FRJ; ++fj)
+                for (int fj = 0; fj < FRJ; ++fj)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    uint2* pv = reinterpret_cast<uint2*>(row + 16 * ((4 * colblk(fj) + g) ^ asw));
-                    const uint2 xv = *pv;
-                    float v[4];
-                    v[0] = fmaf(ca, bf16_lo(xv.x), acc[fi][fj][4 * g + 0]) * alpha;
-                    v[1] = fmaf(ca, bf16_hi(xv.x), acc[fi][fj][4 * g + 1]) * alpha;
-                    v[2] = fmaf(ca, bf16_lo(xv.y), acc[fi][fj][4 * g + 2]) * alpha;
-                    v[3] = fmaf(ca, bf16_hi(xv.y), acc[fi][fj][4 * g + 3]) * alpha;
-                    uint2 ow;
-                    ow.x = pack_bf16x2(v[0], v[1]);
-                    ow.y = pack_bf16x2(v[2], v[3]);
-                    *pv = ow;
-                    if (ROWSTATS) {
-                        const float r0 = bf16_lo(ow.x), r1 = bf16_hi(ow.x), r2 = bf16_lo(ow.y), r3 = bf16_hi(ow.y);
-                        rsq[fi] = fmaf(r0, r0, rsq[fi]);
-                        rsq[fi] = fmaf(r1, r1, rsq[fi]);
-                        rsq[fi] = fmaf(r2, r2, rsq[fi]);
-                        rsq[fi] = fmaf(r3, r3, rsq[fi]);
+                    for (int g = 0; g < 4; ++g) {
+                        uint2* pv = reinterpret_cast<uint2*>(row + 16 * ((4 * colblk(fj) + g) ^ asw));
+                        const uint2 xv = *pv;
+                        float v[4];
+                        v[0] = fmaf(ca, bf16_lo(xv.x), acc[fi][fj][4 * g + 0]);
+                        v[1] = fmaf(ca, bf16_hi(xv.x), acc[fi][fj][4 * g + 1]);
+                        v[2] = fmaf(ca, bf16_lo(xv.y), acc[fi][fj][4 * g + 2]);
+                        v[3] = fmaf(ca, bf16_hi(xv.y), acc[fi][fj][4 * g + 3]);
+                        if constexpr (decltype(scaled)::value) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] *= alpha;
+                        }
+                        uint2 ow;
+                        ow.x = pack_bf16x2(v[0], v[1]);
+                        ow.y = pack_bf16x2(v[2], v[3]);
+                        *pv = ow;
+                        if (ROWSTATS) {
+                            const float r0 = bf16_lo(ow.x), r1 = bf16_hi(ow.x), r2 = bf16_lo(ow.y),
+                                        r3 = bf16_hi(ow.y);
+                            rsq[fi] = fmaf(r0, r0, rsq[fi]);
+                            rsq[fi] = fmaf(r1, r1, rsq[fi]);
+                            rsq[fi] = fmaf(r2, r2, rsq[fi]);
+                            rsq[fi] = fmaf(r3, r3, rsq[fi]);
+                        }
                     }
-                }
-        }
+            }
+        };
+        if (first)
+            own_update(std::true_type{});
+        else
+            own_update(std::false_type{});
         __syncthreads();
     } else {
     uint2 ev[FRI][FRJ][4];
