@@ -413,8 +413,11 @@ static muon_status step_impl(muon_handle* h, float* params, const float* grads, 
                            [&] { return muon::launch_ns_panel(Lg[grp], pl, np, co_all, P.hp.normuon); });
                 if (s != MUON_OK) return s;
             }
-            // the small matrices, after group 0's panel workgroups (which hold a
-            // whole CU each for all iterations) so that they fill the other CUs
+            // the small matrices, every iteration in one launch, after group 0's
+            // panel launch on the same stream: the panels start right after the
+            // momentum, and the small matrices follow while the other groups'
+            // panels still run (a panel workgroup needs a whole CU, so small
+            // workgroups running beside the panels' start would delay them)
             if (k == 0 && grp == 0 && !P.small.empty()) {
                 s = run_on(sg[0], MUON_KERNEL_NS_SMALL, "small-matrix Newton-Schulz kernel", [&] {
                     return muon::launch_ns_small(Lg[0], reinterpret_cast<const int32_t*>(h->ws + P.off_small),
