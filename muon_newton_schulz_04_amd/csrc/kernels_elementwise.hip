@@ -83,7 +83,7 @@ __device__ __forceinline__ float mom_update(float g, float& m, const MomParams& 
 }
 
 // X~ stores: cached (NT = false) when the Gram kernel can still find X~ in
-// L2 / the MALL, nontemporal when the launch writes more X~ than they hold.
+// L2 / the MALL, nontemporal when the group writes more X~ than the MALL holds.
 template <typename XT, bool NT>
 __device__ __forceinline__ void store_x4(XT* dst, float a, float b, float c, float d);
 

@@ -19,7 +19,7 @@ struct LaunchCtx {
     int ew_tiles;             // elementwise tiles of this launch
     int n_active;             // active matrices from `active` on
     void* xt;                 // momentum output X~ (canonical, padded)
-    int xt_nontemporal;       // store X~ nontemporally (the launch writes more X~ than L2 + MALL hold)
+    int xt_nontemporal;       // momentum stores X~ nontemporally (its group writes more X~ than the MALL holds)
     void* x0;                 // ping-pong X buffers
     void* x1;
     void* a;                  // Gram A
