@@ -117,7 +117,8 @@ muon::LaunchCtx make_ctx(const muon_handle* h, hipStream_t stream) {
     L.ew_tiles = (int)P.ew_map.size();
     L.n_active = (int)P.active.size();
     L.xt = ws + P.off_xt;
-    L.xt_nontemporal = 0;  // set per stream group by the step
+    // the whole table as one launch (the step sets this per stream group)
+    L.xt_nontemporal = P.n_groups == 1 ? P.xt_nontemporal[0] : 0;
     L.x0 = ws + P.off_x0;
     L.x1 = ws + P.off_x1;
     L.a = ws + P.off_a;
