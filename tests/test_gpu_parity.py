@@ -86,6 +86,34 @@ def test_ragged_bf16_all_stages(normuon):
     _run_all_stages(w, 3)
 
 
+def _random_table(seed, n_entries):
+    """A seeded mixed table: small (1..64), medium and large sides in both
+    orientations, 256-row panels, every gradient class, lr_mul 0.5 / 1 / 2 and
+    some frozen entries, so that shapes meet every kernel class and edge case
+    together in one plan."""
+    rng = np.random.default_rng(seed)
+    classes = ["spike", "gauss", "student_t", "rank8", "zero"]
+    out = []
+    for _ in range(n_entries):
+        kind = rng.choice(["small", "medium", "large", "panel"], p=[0.35, 0.3, 0.2, 0.15])
+        lo, hi = {"small": (1, 64), "medium": (65, 300), "large": (301, 800), "panel": (257, 1400)}[kind]
+        a, b = int(rng.integers(lo, hi + 1)), int(rng.integers(lo if kind == "panel" else 1, hi + 1))
+        if kind == "panel":
+            a = 256  # and the other side > 256: one 256-row panel
+        r, c = (a, b) if rng.random() < 0.5 else (b, a)
+        out.append((r, c, int(rng.integers(1, 3)), str(rng.choice(classes, p=[0.3, 0.25, 0.2, 0.15, 0.1])),
+                    float(rng.choice([0.5, 1.0, 2.0])), int(rng.random() < 0.1)))
+    return out
+
+
+@pytest.mark.parametrize("normuon", [0, 1])
+def test_random_mixed_tables_all_stages(normuon):
+    shapes = _random_table(20261203 + normuon, 14)
+    _say(f"[case] random table (normuon={normuon}): {shapes}")
+    w = custom_workload(170 + normuon, shapes, steps=2, normuon=normuon, lr=0.05, weight_decay=0.05 * normuon)
+    _run_all_stages(w, 2)
+
+
 # matrices that are one 256-row panel (every iteration in one workgroup,
 # A and B in LDS), next to one just beyond the panel kernel's limit
 PANEL = [
