@@ -106,12 +106,14 @@ def _random_table(seed, n_entries):
     return out
 
 
-@pytest.mark.parametrize("normuon", [0, 1])
-def test_random_mixed_tables_all_stages(normuon):
-    shapes = _random_table(20261203 + normuon, 14)
-    _say(f"[case] random table (normuon={normuon}): {shapes}")
-    w = custom_workload(170 + normuon, shapes, steps=2, normuon=normuon, lr=0.05, weight_decay=0.05 * normuon)
-    _run_all_stages(w, 2)
+@pytest.mark.parametrize("case, precision, normuon, groups", [(0, "bf16", 0, 3), (1, "bf16", 1, 3),
+                                                            (2, "fp32", 1, 2), (3, "bf16", 0, 4)])
+def test_random_mixed_tables_all_stages(case, precision, normuon, groups):
+    shapes = _random_table(20261203 + case, 14)
+    _say(f"[case] random table {case} ({precision}, normuon={normuon}, {groups} stream groups): {shapes}")
+    w = custom_workload(170 + case, shapes, steps=2, ns_precision=precision, normuon=normuon, lr=0.05,
+                        weight_decay=0.05 * normuon)
+    _run_all_stages(w, 2, stream_groups=groups)
 
 
 # matrices that are one 256-row panel (every iteration in one workgroup,
