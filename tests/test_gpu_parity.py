@@ -236,7 +236,9 @@ def test_step_captured_in_a_hip_graph_replays_like_eager():
     # muon_step allocates nothing, never synchronises and records no memset,
     # and its two-stream fork / join is event-based, so a caller can capture it
     # in a HIP graph; every replay must equal the eager step on the same state
-    w = custom_workload(111, LARGE_TILES + [(64, 64, 3, "rank8")], steps=1, lr=0.05, weight_decay=0.1)
+    # (tiled, small and one-panel matrices: every kind of launch the step makes)
+    w = custom_workload(111, LARGE_TILES + [(64, 64, 3, "rank8"), (256, 512, 2, "spike")], steps=1, lr=0.05,
+                        weight_decay=0.1)
     run = GpuRun(w)
     run.load_grads(0)
     run.step()  # past the first-step paths
@@ -428,7 +430,8 @@ def gen0(w):
 
 
 def test_determinism_and_batch_independence():
-    shapes = [(200, 200, 2, "spike"), (136, 520, 1, "spike"), (520, 136, 1, "spike"), (64, 64, 2, "rank8")]
+    shapes = [(200, 200, 2, "spike"), (136, 520, 1, "spike"), (520, 136, 1, "spike"), (64, 64, 2, "rank8"),
+              (256, 512, 1, "spike")]
     w = custom_workload(104, shapes, steps=2, normuon=1)
     r1, r2 = GpuRun(w), GpuRun(w)
     for t in range(2):
