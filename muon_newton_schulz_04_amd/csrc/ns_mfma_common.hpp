@@ -24,14 +24,17 @@ __device__ __forceinline__ bf16x4 tr_read(const char* p) {
 // flight (vmcnt(0)) before LDS reads it cannot prove disjoint, which undoes
 // the ring; the kernel orders the ring itself with explicit vmcnt waits and
 // barriers, and every such load has completed before any compiler-managed
-// vector memory wait (the epilogue) is reached. The asm declares M0
-// clobbered, so the compiler keeps no value of its own there across it.
+// vector memory wait (the epilogue) is reached.
+// M0: the asm sets it itself, in the same block, right before the load. The
+// compiler reserves M0 and does not honour a clobber of it, so what makes
+// this safe is that the kernels built on this helper hold no M0 value of the
+// compiler's own: their gfx950 assembly has no instruction that reads or
+// writes M0 besides these pairs (a host test compiles them and checks that).
 __device__ __forceinline__ void dma16(u32x4 r, char* lds, int voff, int soff) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)lds);
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "v"(voff), "s"(r), "s"(soff), "s"(m0v)
-                 : "m0");
+                 : "v"(voff), "s"(r), "s"(soff), "s"(m0v));
 }
 
 // Buffer resource of `bytes` bytes at `base` (stride 0, raw buffer): word 0
