@@ -320,6 +320,12 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
         using ICN = std::integral_constant<int, NF>;
         if constexpr (LOAD) dma_stage(kt + D, NL);
         if constexpr (decltype(spare_c)::value) dma_own(smem + SPARE_OFF, 0, NSP_C{});  // own rows 0 .. NSP-1
+        // the last slice: own rows NSP .. NSP + NRB - 1 into the ring buffer it
+        // leaves free (the previous slice's, which every wave finished
+        // reading before that slice's barrier), so that they land under this
+        // slice's MFMAs (nk >= 2: the second-to-last slice sent rows 0 .. NSP-1)
+        if constexpr (OWN && WAIT < 0)
+            dma_own(smem + ((kt + 1) % NBUF) * LY::STAGE, NSP, std::integral_constant<int, NRB>{});
 #pragma unroll
         for (int ks = 0; ks < NKS - 1; ++ks) {
             const int set = ks & 1;
@@ -349,10 +355,6 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             }
             if (NREAD > NF / 2) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NF / 2, 0);
         } else {
-            if constexpr (OWN) {
-                // nk >= 2: the second-to-last slice already sent rows 0 .. NSP-1
-                dma_own(smem + ((kt + 1) % NBUF) * LY::STAGE, NSP, std::integral_constant<int, NRB>{});
-            }
             mfma_block(SL, IC0{}, ICN{}, mask_c);
             __syncthreads();
         }
