@@ -210,7 +210,7 @@ def _kernel_class(name: str) -> str:
         return "copy"
     if "k_ns_big<" in name or "k_ns<" in name:
         mode = name.split("<", 1)[1].split(">", 1)[0].split(",")
-        return {"0": "gram", "1": "poly", "2": "update"}[mode[-2].strip() if "big" in name else mode[2].strip()]
+        return {"0": "gram", "1": "poly", "2": "update"}[mode[2].strip()]
     for k in ("ns_small", "ns_panel", "momentum", "apply"):
         if "k_" + k in name:
             return k
@@ -221,10 +221,10 @@ def _short_kernel(name: str) -> str:
     """A readable label for a libmuon kernel from its demangled name."""
     import re
     mode = {"0": "GRAM", "1": "POLY", "2": "UPDATE"}
-    m = re.search(r"k_ns_big<(\d+), (\d+), (\d), (\w+)>", name)
+    m = re.search(r"k_ns_big<(\d+), (\d+), (\d), (\w+)(?:, (\w+))?>", name)
     if m:
         return (f"k_ns_big {mode[m.group(3)]} T={m.group(1)} waves={2 * int(m.group(2))}"
-                + (" +rowstats" if m.group(4) == "true" else ""))
+                + (" +rowstats" if m.group(4) == "true" else "") + (" +nt" if m.group(5) == "true" else ""))
     m = re.search(r"k_ns<([^,]+), (\d+), (\d)>", name)
     if m:
         return f"k_ns<{'bf16' if 'bf' in m.group(1) else 'f32'}> {mode[m.group(3)]} T={m.group(2)}"

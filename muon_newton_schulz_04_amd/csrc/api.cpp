@@ -119,6 +119,7 @@ muon::LaunchCtx make_ctx(const muon_handle* h, hipStream_t stream) {
     L.xt = ws + P.off_xt;
     // the whole table as one launch (the step sets this per stream group)
     L.xt_nontemporal = P.n_groups == 1 ? P.xt_nontemporal[0] : 0;
+    L.ab_nontemporal = P.n_groups == 1 ? P.ab_nontemporal[0] : 0;
     L.x0 = ws + P.off_x0;
     L.x1 = ws + P.off_x1;
     L.a = ws + P.off_a;
@@ -380,6 +381,7 @@ static muon_status step_impl(muon_handle* h, float* params, const float* grads, 
         Lg[grp].ew_tile0 = P.ew_begin[grp];
         Lg[grp].ew_tiles = P.ew_begin[grp + 1] - P.ew_begin[grp];
         Lg[grp].xt_nontemporal = P.xt_nontemporal[grp];
+        Lg[grp].ab_nontemporal = P.ab_nontemporal[grp];
         Lg[grp].active = L.active + P.act_begin[grp];
         Lg[grp].n_active = P.act_begin[grp + 1] - P.act_begin[grp];
     }

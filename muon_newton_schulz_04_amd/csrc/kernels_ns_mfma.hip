@@ -70,7 +70,9 @@ struct Layout {
     static_assert(BK * XROWB == KTILE, "X tile and k-contiguous tile have the same size");
 };
 
-template <int T, int WN, int MODE, bool ROWSTATS>
+// NTOUT (Gram, polynomial): store the output tile and its mirror
+// nontemporally (chosen per stream group; see the tile store below)
+template <int T, int WN, int MODE, bool ROWSTATS, bool NTOUT>
 __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__ mats,
                                                      const TileWork* __restrict__ work, const bf16* __restrict__ xin,
                                                      const bf16* __restrict__ ain, bf16* __restrict__ out, float ca,
@@ -579,7 +581,12 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
     // the tile itself: each thread moves 16-byte row chunks, a wave covers
     // whole rows. The update's output is stored nontemporally: a round of
     // tiles writes about as much as an XCD's L2 holds, and normal stores
-    // would push out the B and X panels the next round reads.
+    // would push out the B and X panels the next round reads. The Gram's and
+    // the polynomial's outputs (and their mirrors) are too in the NTOUT
+    // instances, launched when their stream group's A is larger than the
+    // MALL, so that the next stage would find little of them in cache. (A
+    // runtime choice between the two stores does not survive: the compiler
+    // merges the two branches into one store and drops the hint.)
     {
         bf16* obase = MODE == NS_UPDATE ? out + d.x_off + (int64_t)i0 * d.n_pad + j0
                                         : out + d.a_off + (int64_t)i0 * d.m_pad + j0;
@@ -599,7 +606,7 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
                 const uint2 up = lds64(r * EROW + 16 * c + 8);
                 wv = u32x4{lo.x, lo.y, up.x, up.y};
             }
-            if (MODE == NS_UPDATE)
+            if constexpr (MODE == NS_UPDATE || NTOUT)
                 __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(obase + (int64_t)r * ld + 8 * c));
             else
                 *reinterpret_cast<u32x4*>(obase + (int64_t)r * ld + 8 * c) = wv;
@@ -628,8 +635,13 @@ __global__ __launch_bounds__(128 * WN) void k_ns_big(const MatDesc* __restrict__
             const bf16x4 lo = tr_read(smem + (IB + sup_row) * EROW + 2 * JB);
             const bf16x4 up = tr_read(smem + (IB + sup_row + 4) * EROW + 2 * JB);
             const bf16x8 v = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-            if (!same || ((JB + rc) >> 5) > ((IB + 32 * G + 8 * rq) >> 5))
-                *reinterpret_cast<bf16x8*>(mbase + (int64_t)(JB + rc) * d.m_pad + IB + 32 * G + 8 * rq) = v;
+            if (!same || ((JB + rc) >> 5) > ((IB + 32 * G + 8 * rq) >> 5)) {
+                bf16x8* dst = reinterpret_cast<bf16x8*>(mbase + (int64_t)(JB + rc) * d.m_pad + IB + 32 * G + 8 * rq);
+                if constexpr (NTOUT)
+                    __builtin_nontemporal_store(v, dst);
+                else
+                    *dst = v;
+            }
         }
     }
 
@@ -664,19 +676,27 @@ hipError_t launch_big_T(const LaunchCtx& L, const GemmList& G, int mode, const v
     const bf16* a = (const bf16*)ain;
     bf16* o = (bf16*)out;
     constexpr int NT = 128 * WN;
-    if (mode == NS_GRAM)
-        k_ns_big<T, WN, NS_GRAM, false><<<n, NT, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials,
-                                                                L.ss, L.scale, L.status, eps, L.rowpart);
-    else if (mode == NS_POLY)
-        k_ns_big<T, WN, NS_POLY, false><<<n, NT, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first, L.partials,
-                                                                L.ss, L.scale, L.status, eps, L.rowpart);
-    else if (rowstats)
-        k_ns_big<T, WN, NS_UPDATE, true><<<n, NT, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first,
-                                                                 L.partials, L.ss, L.scale, L.status, eps, L.rowpart);
-    else
-        k_ns_big<T, WN, NS_UPDATE, false><<<n, NT, 0, L.stream>>>(L.mats, wl, x, a, o, ca, cb, cc, first,
-                                                                  L.partials, L.ss, L.scale, L.status, eps,
-                                                                  L.rowpart);
+#define K_NS_BIG_ARGS \
+    L.mats, wl, x, a, o, ca, cb, cc, first, L.partials, L.ss, L.scale, L.status, eps, L.rowpart
+    // the Gram's and the polynomial's output stores are nontemporal for a
+    // stream group whose A exceeds the MALL (the update's are in any case)
+    const bool nt = L.ab_nontemporal != 0;
+    if (mode == NS_GRAM) {
+        if (nt)
+            k_ns_big<T, WN, NS_GRAM, false, true><<<n, NT, 0, L.stream>>>(K_NS_BIG_ARGS);
+        else
+            k_ns_big<T, WN, NS_GRAM, false, false><<<n, NT, 0, L.stream>>>(K_NS_BIG_ARGS);
+    } else if (mode == NS_POLY) {
+        if (nt)
+            k_ns_big<T, WN, NS_POLY, false, true><<<n, NT, 0, L.stream>>>(K_NS_BIG_ARGS);
+        else
+            k_ns_big<T, WN, NS_POLY, false, false><<<n, NT, 0, L.stream>>>(K_NS_BIG_ARGS);
+    } else if (rowstats) {
+        k_ns_big<T, WN, NS_UPDATE, true, false><<<n, NT, 0, L.stream>>>(K_NS_BIG_ARGS);
+    } else {
+        k_ns_big<T, WN, NS_UPDATE, false, false><<<n, NT, 0, L.stream>>>(K_NS_BIG_ARGS);
+    }
+#undef K_NS_BIG_ARGS
     return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ struct LaunchCtx {
     int n_active;             // active matrices from `active` on
     void* xt;                 // momentum output X~ (canonical, padded)
     int xt_nontemporal;       // momentum stores X~ nontemporally (its group writes more X~ than the MALL holds)
+    int ab_nontemporal;       // Gram / polynomial store A, B nontemporally (the group's A exceeds the MALL)
     void* x0;                 // ping-pong X buffers
     void* x1;
     void* a;                  // Gram A

@@ -357,6 +357,17 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
         P.lists.push_back(std::move(L));
     }
 
+    // ---- Gram / polynomial output stores per group (see kAbCachedMax) ----
+    {
+        int64_t ab_bytes[kMaxGroups] = {};
+        for (int32_t mi : P.active) {
+            const MatDesc& d = P.mats[mi];
+            if (P.is_small(d) || P.is_panel(d)) continue;
+            ab_bytes[group_of[mi]] += (int64_t)d.m_pad * d.m_pad * P.esize;
+        }
+        for (int grp = 0; grp < P.n_groups; ++grp) P.ab_nontemporal[grp] = ab_bytes[grp] > kAbCachedMax ? 1 : 0;
+    }
+
     // ---- workspace layout ----
     size_t off = 0;
     auto take = [&](size_t bytes) {

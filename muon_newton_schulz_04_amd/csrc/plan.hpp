@@ -29,6 +29,12 @@ constexpr int kCusPerXcd = 32;
 // caches anyway, and the streaming stores run the pass 1.5% (runs) to 9%
 // (transposed tiles) faster.
 constexpr int64_t kXtCachedMax = (int64_t)256 << 20;
+// Likewise for the Gram and polynomial outputs: a group whose A (an m_pad x
+// m_pad tile set per tiled matrix) is larger than the MALL stores A and B,
+// mirrors included, nontemporally. The next stage finds little of them in
+// cache then, and the streaming stores leave the X and B panels there. Groups
+// that fit keep cached stores, which the next stage reads from the MALL.
+constexpr int64_t kAbCachedMax = (int64_t)256 << 20;
 
 struct TileList {
     int T = 0;
@@ -55,6 +61,7 @@ struct Plan {
     int act_begin[kMaxGroups + 1] = {};
     int ew_begin[kMaxGroups + 1] = {};
     int xt_nontemporal[kMaxGroups] = {};  // per group: momentum stores X~ nontemporally
+    int ab_nontemporal[kMaxGroups] = {};  // per group: Gram / polynomial store A, B nontemporally
     std::vector<int32_t> panel;         // one-panel matrices, group by group
     int panel_begin[kMaxGroups + 1] = {};
     size_t off_panel = 0;

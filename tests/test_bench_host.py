@@ -20,6 +20,12 @@ NAMES = {
     "muon::(anonymous namespace)::k_ns_big<256, 4, 1, false>(muon::MatDesc const*)": ("poly", "k_ns_big POLY T=256 waves=8"),
     "muon::(anonymous namespace)::k_ns_big<128, 2, 2, true>(muon::MatDesc const*)":
         ("update", "k_ns_big UPDATE T=128 waves=4 +rowstats"),
+    "muon::(anonymous namespace)::k_ns_big<256, 4, 0, false, true>(muon::MatDesc const*)":
+        ("gram", "k_ns_big GRAM T=256 waves=8 +nt"),
+    "muon::(anonymous namespace)::k_ns_big<256, 4, 1, false, false>(muon::MatDesc const*)":
+        ("poly", "k_ns_big POLY T=256 waves=8"),
+    "muon::(anonymous namespace)::k_ns_big<256, 4, 2, true, false>(muon::MatDesc const*)":
+        ("update", "k_ns_big UPDATE T=256 waves=8 +rowstats"),
     "muon::(anonymous namespace)::k_ns<float, 64, 2>(muon::MatDesc const*)": ("update", "k_ns<f32> UPDATE T=64"),
     "muon::(anonymous namespace)::k_momentum<__bf16>(muon::MatDesc const*)": ("momentum", "k_momentum"),
     "muon::(anonymous namespace)::k_apply<__bf16>(muon::MatDesc const*)": ("apply", "k_apply"),

@@ -334,6 +334,36 @@ def test_fp32_group_larger_than_the_mall():
         assert_worst(worst, fp32=True)
 
 
+def test_bf16_group_whose_gram_output_exceeds_the_mall():
+    # one stream group whose Gram output A (34 x 2048^2 bf16 = 285 MB) is larger
+    # than the 256 MB MALL: the Gram and polynomial kernels store A and B, their
+    # mirrors included, nontemporally (as the momentum kernel does X~). The
+    # first and last matrix are checked against the oracle, and the last
+    # iteration's A and B of both must still be exactly symmetric
+    w = custom_workload(119, [(2048, 2048, 34, "spike")], steps=2, lr=0.05)
+    _say(f"[case] {w.name}: {w.num_matrices} matrices, {w.total} elements, one stream group")
+    run = GpuRun(w, stream_groups=1)
+    sample = [0, 33]
+    orc_m = {gi: np.zeros((run.subs[gi][4], run.subs[gi][5])) for gi in sample}
+    for t in range(w.steps):
+        p_prev, v_prev = snapshot(run, sample)
+        g = run.load_grads(t)
+        run.step()
+        worst = check_stages(run, t, sample, grads_host=g, p_prev=p_prev, v_prev=v_prev, orc_m=orc_m)
+        _say(f"  step {t}: {worst}")
+        assert_worst(worst)
+    A_all = run.H.view(B.MUON_VIEW_GRAM, torch.bfloat16)
+    P_all = run.H.view(B.MUON_VIEW_POLY, torch.bfloat16)
+    for gi in sample:
+        L = run.lay[gi]
+        sz = L.m_pad * L.m_pad
+        A = A_all[L.gram_offset:L.gram_offset + sz].view(L.m_pad, L.m_pad)
+        P = P_all[L.gram_offset:L.gram_offset + sz].view(L.m_pad, L.m_pad)
+        assert torch.equal(A, A.t().contiguous()), f"A of matrix {gi} not symmetric"
+        assert torch.equal(P, P.t().contiguous()), f"B of matrix {gi} not symmetric"
+    assert np.all(run.scalars(B.MUON_VIEW_STATUS) == 0)
+
+
 def test_heavy_ball_and_weight_decay_and_steps():
     # heavy-ball momentum, Nesterov off, decoupled weight decay, 7 NS steps with
     # a per-iteration coefficient schedule whose last step is the cubic
