@@ -435,6 +435,7 @@ def measure(w, steps: int, warmup: int, kernel_steps: int, pool: int, stream_gro
     fp32 = w.ns_precision == "fp32"
     peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
     res = {"workload": w.name, "steps": steps, "warmup": warmup, "grad_sets": pool, "ms_per_step": ms,
+           "stream_groups": int(work.launches[B.MUON_KERNEL_MOMENTUM]),
            "step_ms": _stats(per_step), "wall_s": wall, "ns_alg_gflop_per_step": ns_flops / 1e9,
            "ns_tflops_step": ns_flops / (ms * 1e-3) / 1e12, "pct_peak_step": ns_flops / (ms * 1e-3) / 1e12 / peak * 100,
            "peak_tflops": peak, "dtype": "fp32" if fp32 else "bf16", "elements": w.total,
@@ -509,7 +510,8 @@ def main() -> int:
     ap.add_argument("--no-events", action="store_true", help="do not time kernels with events")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="measure only the headline workload (no per-config section)")
-    ap.add_argument("--stream-groups", type=int, default=3, help="stream groups of the timed pass (1 .. 4)")
+    ap.add_argument("--stream-groups", type=int, default=0,
+                    help="stream groups of the timed pass (0: the library's choice, 1 .. 4)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB once per pass (HBM counter calibration)")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
@@ -586,7 +588,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "layers": len(w.entries) // 3 if args.config in (1, 2, 3) else None,
                    "matrices": w.num_matrices, "elements": w.total, "ns_steps": w.ns_steps,
-                   "ns_precision": w.ns_precision, "normuon": w.normuon, "parallelism": "single GPU"},
+                   "ns_precision": w.ns_precision, "normuon": w.normuon, "parallelism": "single GPU",
+                   "stream_groups": head["stream_groups"]},
         "step_ms": head["step_ms"],
         "ns_alg_gflop_per_step": head["ns_alg_gflop_per_step"],
         "ns_tflops_kernels": head.get("ns_tflops_kernels"),

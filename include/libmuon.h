@@ -84,10 +84,13 @@ enum { MUON_MOMENTUM_LERP = 0, MUON_MOMENTUM_HEAVY_BALL = 1 };
  *  ([P2] change 2); HEAVY_BALL: m <- beta m + g, Nesterov u = g + beta m
  *  ([P4] Muon source). ns_precision BF16: bf16 MFMA operands with fp32
  *  accumulation; FP32: fp32 throughout (debug / reference mode).
- *  stream_groups (not a method parameter; 1 .. 4, default 3): G > 1 lets
+ *  stream_groups (not a method parameter; 0 .. 4, default 0): G > 1 lets
  *  muon_step split the tiled matrices into up to G cost-balanced groups, at
  *  least 2 matrices per group, when their update output is at most 262144
- *  tiles of 64 x 64 (a few tile rounds of the GPU per launch). Each group
+ *  tiles of 64 x 64 (a few tile rounds of the GPU per launch). 0 lets the
+ *  library choose: 3 when the update output is at least 4096 such tiles
+ *  (one round of 256 x 256 tiles on 256 CUs), 1 for smaller steps, whose
+ *  launches are latency-bound. Each group
  *  runs its chain (momentum, Newton–Schulz, NorMuon, update) on its own
  *  stream: group 0 on the caller's stream, group g > 0 on a default-priority
  *  stream the handle owns, started after group g - 1's momentum and joined

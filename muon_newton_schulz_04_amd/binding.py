@@ -286,7 +286,7 @@ def check(status: int, h=None, what: str = "") -> None:
 
 def make_hparams(momentum=0.95, nesterov=1, momentum_kind=MUON_MOMENTUM_LERP, ns_steps=5, coeffs=None,
                  ns_eps=1e-7, precision="bf16", normuon=0, normuon_beta2=0.95, normuon_eps=1e-10,
-                 weight_decay=0.0, stream_groups=3) -> muon_hparams:
+                 weight_decay=0.0, stream_groups=0) -> muon_hparams:
     hp = muon_hparams_default()
     hp.momentum = momentum
     hp.nesterov = nesterov

@@ -63,7 +63,7 @@ muon_status check_hparams(const muon_hparams* hp, std::string* err) {
         return bad("normuon_beta2 must be in [0, 1]");
     if (!finite(hp->normuon_eps) || hp->normuon_eps < 0.f) return bad("normuon_eps must be finite and >= 0");
     if (!finite(hp->weight_decay)) return bad("weight_decay must be finite");
-    if (hp->stream_groups < 1 || hp->stream_groups > kMaxGroups) return bad("stream_groups must be in [1, 4]");
+    if (hp->stream_groups < 0 || hp->stream_groups > kMaxGroups) return bad("stream_groups must be in [0, 4]");
     return MUON_OK;
 }
 
@@ -256,7 +256,9 @@ muon_status build_plan(const muon_matrix* table, int32_t n, const muon_hparams* 
             cost.push_back({m * (m + 1) * nn + m * (m + 1) * m + 2 * m * m * nn, mi});
             tiles64 += (int64_t)(d.m_pad / 64) * (d.n_pad / 64);
         }
-        const int ng = std::min<int>(P.hp.stream_groups, (int)(cost.size() / kMinSplit));
+        const int want = P.hp.stream_groups > 0 ? P.hp.stream_groups
+                         : (tiles64 >= kAutoSplitMinTiles64 ? kAutoGroups : 1);
+        const int ng = std::min<int>(want, (int)(cost.size() / kMinSplit));
         if (ng > 1 && tiles64 <= kMaxSplitTiles64) {
             P.n_groups = ng;
             std::stable_sort(cost.begin(), cost.end(),
@@ -423,5 +425,5 @@ extern "C" void muon_hparams_default(muon_hparams* hp) {
     hp->normuon_beta2 = 0.95f;
     hp->normuon_eps = 1e-10f;
     hp->weight_decay = 0.0f;
-    hp->stream_groups = 3;
+    hp->stream_groups = 0;
 }

@@ -54,9 +54,11 @@ def exact_bound(ce: float, iterations: int) -> float:
 
 
 def hp_for(w, **over):
+    # three stream groups unless a test asks otherwise: the library would keep
+    # these small tables in one group, and the tests exercise the split path
     kw = dict(momentum=w.momentum, nesterov=w.nesterov, ns_steps=w.ns_steps, precision=w.ns_precision,
               normuon=w.normuon, normuon_beta2=w.normuon_beta2, normuon_eps=w.normuon_eps,
-              weight_decay=w.weight_decay)
+              weight_decay=w.weight_decay, stream_groups=3)
     kw.update(over)
     return B.make_hparams(**kw)
 

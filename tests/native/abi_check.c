@@ -168,7 +168,11 @@ int main(void) {
         ws(t, 1, &bad, &st);
         EXPECT(st == MUON_E_INVALID_ARG);
         muon_hparams_default(&bad);
-        bad.stream_groups = 0;
+        bad.stream_groups = -1; /* 0 is the library's choice, 1 .. 4 explicit */
+        ws(t, 1, &bad, &st);
+        EXPECT(st == MUON_E_INVALID_ARG);
+        muon_hparams_default(&bad);
+        bad.stream_groups = 5;
         ws(t, 1, &bad, &st);
         EXPECT(st == MUON_E_INVALID_ARG);
         muon_hparams_default(&bad);

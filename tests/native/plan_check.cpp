@@ -133,6 +133,31 @@ int main() {
         for (const MatDesc& d : P.mats) EXPECT(d.T == 256 && d.m_pad == 768);
     }
     {
+        // stream_groups = 0: the planner chooses three groups from 4096 update
+        // tiles of 64 x 64 on (one round of 256-tiles on the GPU), one below
+        Table tiny, mid, big, body124m;
+        tiny.body(1, 128);       // 48 tiles
+        mid.body(4, 512);        // 3072 tiles
+        big.body(4, 768);        // 6912 tiles
+        body124m.body(12, 768);  // 20736 tiles
+        EXPECT(plan(tiny, 0, 0, &P) && P.n_groups == 1);
+        EXPECT(plan(tiny, 0, 1, &P) && P.n_groups == 1);
+        EXPECT(plan(mid, 0, 0, &P) && P.n_groups == 1);
+        check_lists(P);
+        EXPECT(plan(big, 0, 0, &P) && P.n_groups == 3);
+        check_lists(P);
+        EXPECT(plan(body124m, 0, 0, &P) && P.n_groups == 3);
+        // an explicit count is kept for small steps too (at least two tiled
+        // matrices per group)
+        EXPECT(plan(tiny, 3, 0, &P) && P.n_groups == 3);
+        check_lists(P);
+        // the stress batch's one-panel matrices count: 192 x 64 tiles
+        Table stress;
+        stress.add(64, 64, 4096);
+        stress.add(256, 1024, 192);
+        EXPECT(plan(stress, 0, 0, &P) && P.n_groups == 3);
+    }
+    {
         // the same body in one group: X~ (170 MB) and A (85 MB) fit the MALL
         Table tb;
         tb.body(12, 768);

@@ -50,7 +50,7 @@ def test_hparams_default_values():
         assert (round(a, 4), round(b, 4), round(c, 4)) == (3.4445, -4.775, 2.0315)
     assert math.isclose(hp.ns_eps, 1e-7, rel_tol=1e-6)
     assert hp.normuon == 0 and math.isclose(hp.normuon_eps, 1e-10, rel_tol=1e-6)
-    assert hp.stream_groups == 3
+    assert hp.stream_groups == 0  # the library chooses (one group for small steps, else three)
 
 
 def _ws(entries, hp=None):
@@ -108,9 +108,10 @@ def test_validation_errors():
     bad = B.muon_hparams_default()
     bad.ns_precision = 3
     assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0)], bad)[0] == B.MUON_E_INVALID_ARG
-    bad = B.muon_hparams_default()
-    bad.stream_groups = 5
-    assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0)], bad)[0] == B.MUON_E_INVALID_ARG
+    for groups in (5, -1):
+        bad = B.muon_hparams_default()
+        bad.stream_groups = groups
+        assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0)], bad)[0] == B.MUON_E_INVALID_ARG
     # adjacent (touching) entries are fine; empty table is fine
     assert _ws([M(4, 4, 1, 0, 1.0, 1.0, 0, 0), M(4, 4, 1, 16, 1.0, 1.0, 0, 0)], hp)[0] == B.MUON_OK
     assert _ws([], hp)[0] == B.MUON_OK

@@ -215,16 +215,19 @@ def test_newton_schulz_step_counts_convergent_tail(ns_steps):
 
 def test_stream_groups_give_identical_results():
     # the 9 tiled matrices split over 2, 3 or 4 streams, or all on the
-    # caller's stream: the same kernels on the same tiles, so bit-identical
+    # caller's stream (also the library's own choice, 0, for a step this
+    # small): the same kernels on the same tiles, so bit-identical
     w = custom_workload(110, LARGE_TILES + [(200, 300, 2, "spike"), (64, 64, 3, "rank8"), (256, 512, 2, "spike")],
                         steps=2, lr=0.05,
                         weight_decay=0.1, normuon=1)
-    runs = [GpuRun(w, stream_groups=g) for g in (1, 2, 3, 4)]
+    groups = (1, 0, 2, 3, 4)
+    runs = [GpuRun(w, stream_groups=g) for g in groups]
+    assert [int(B.muon_work_stats(r.H.h).launches[B.MUON_KERNEL_MOMENTUM]) for r in runs] == [1, 1, 2, 3, 4]
     for t in range(2):
         for r in runs:
             r.load_grads(t)
             r.step()
-        for g, r in enumerate(runs[1:], start=2):
+        for g, r in zip(groups[1:], runs[1:]):
             for name in ("params", "mom"):
                 assert torch.equal(getattr(runs[0], name), getattr(r, name)), \
                     f"step {t}: {name} differs between one and {g} stream groups"
