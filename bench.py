@@ -150,6 +150,50 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str, workload_id: int 
     return out
 
 
+LDS_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS")
+
+
+def lds_summary(pmc_dir: str, workload_id: int) -> dict:
+    """LDS behaviour of each kernel class from one rocprofv3 --pmc run of
+    SQ_LDS_BANK_CONFLICT, SQ_LDS_ADDR_CONFLICT, SQ_LDS_IDX_ACTIVE and
+    SQ_INSTS_LDS: the cycles LDS is stalled by bank (and address) conflicts
+    as a share of the cycles it spends on indexed (ds_*) operations, and the
+    LDS instructions issued; medians over the largest-grid dispatches of each
+    class (the one-stream kernel pass). The direct-to-LDS loads of the NS
+    kernels are not indexed operations and are not counted here."""
+    import statistics
+    from workloads import get_workload
+    w = get_workload(workload_id)
+    per = {}
+    for r in _pmc_rows(pmc_dir):
+        key = _kernel_class(r["Kernel_Name"])
+        if not key or key == "copy":
+            continue
+        d = per.setdefault(key, {}).setdefault(int(r["Grid_Size"]), {})
+        d.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    sfx, cfg, lim = _pmc_args(workload_id)
+    out = {"workload": w.name, "source_hash": _kernel_source_hash(),
+           "commands": [f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL {lim} rocprofv3 --pmc "
+                        + " ".join(LDS_COUNTERS) + f" -f csv -d $REPO/gpurun_out/pmc_lds{sfx} -o run -- python3 "
+                        f"$REPO/bench.py{cfg} --steps 3 --warmup 1 --no-cpu-baseline",
+                        f"python3 bench.py{cfg} --pmc-lds-summary gpurun_out/pmc_lds{sfx}"],
+           "note": "bank_conflict_pct = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE x 100 (both summed over the "
+                   "GPU); addr_conflict_pct likewise for SQ_LDS_ADDR_CONFLICT; lds_insts = SQ_INSTS_LDS",
+           "kernels": {}}
+    for key, grids in sorted(per.items()):
+        launches = [d for d in grids[max(grids)].values() if all(c in d for c in LDS_COUNTERS)]
+        if not launches:
+            continue
+        act = statistics.median(d["SQ_LDS_IDX_ACTIVE"] for d in launches)
+        bank = statistics.median(d["SQ_LDS_BANK_CONFLICT"] for d in launches)
+        addr = statistics.median(d["SQ_LDS_ADDR_CONFLICT"] for d in launches)
+        out["kernels"][key] = {"dispatches": len(launches), "lds_idx_active_cycles": act,
+                               "bank_conflict_cycles": bank, "bank_conflict_pct": 100.0 * bank / act if act else None,
+                               "addr_conflict_cycles": addr, "addr_conflict_pct": 100.0 * addr / act if act else None,
+                               "lds_insts": statistics.median(d["SQ_INSTS_LDS"] for d in launches)}
+    return out
+
+
 def _ns_alg_flops(workload) -> dict:
     """Algorithmic FLOP of one GRAM / POLY / UPDATE launch over every active
     bf16 matrix of a workload (symmetric Gram and A A count m(m+1) k)."""
@@ -519,6 +563,9 @@ def main() -> int:
     ap.add_argument("--pmc-mfma-summary", metavar="PMC_DIR",
                     help="summarise a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and "
                          "SQ_INSTS_VALU_MFMA_MOPS_BF16 into profiles/mfma_<workload>.json and exit")
+    ap.add_argument("--pmc-lds-summary", metavar="PMC_DIR",
+                    help="summarise a rocprofv3 --pmc run of " + ", ".join(LDS_COUNTERS)
+                         + " into profiles/lds_<workload>.json and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into "
                          "profiles/traffic_<workload>.json and exit")
@@ -536,6 +583,14 @@ def main() -> int:
     if args.pmc_mfma_summary:
         t = mfma_summary(args.pmc_mfma_summary, args.config)
         path = os.path.join(ROOT, "profiles", f"mfma_{t['workload']}.json")
+        with open(path, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t, indent=1))
+        return 0
+
+    if args.pmc_lds_summary:
+        t = lds_summary(args.pmc_lds_summary, args.config)
+        path = os.path.join(ROOT, "profiles", f"lds_{t['workload']}.json")
         with open(path, "w") as f:
             json.dump(t, f, indent=1)
         print(json.dumps(t, indent=1))

@@ -79,6 +79,15 @@ __device__ __forceinline__ int opaque(int x) {
 __device__ __forceinline__ int res_off(int r, int chunk) { return r * RROW + 16 * (chunk ^ (r & 15)); }
 // the bf16 of row r, column c (with c % 4 == 0 also the 8 bytes of columns c .. c+3)
 __device__ __forceinline__ int res_elem(int r, int c) { return res_off(r, c >> 3) + 2 * (c & 7); }
+// Update slices of X (512-byte rows): chunk c of row r at c ^ xsw(r). Bits
+// 2-3 (r & 3) put the 4 rows a 16-lane transposing read touches in 4 distinct
+// 64-byte bank windows. Bit 0 (row bit 3) permutes chunks inside a window and
+// spreads the a X reads (one 8-byte piece from each of 32 consecutive rows)
+// over 8 16-byte slots instead of 4. xsw reads only row bits 0, 1 and 3,
+// which adding 4 (to a row with bit 2 clear) or 16 leaves alone: the two
+// halves of a transposing read and the two 16-row halves of a slice share one
+// offset.
+__device__ __forceinline__ int xsw(int r) { return 4 * (r & 3) + ((r >> 3) & 1); }
 
 template <bool ROWSTATS>
 __global__ __launch_bounds__(PNT) void k_ns_panel(const MatDesc* __restrict__ mats, const int32_t* __restrict__ list,
@@ -183,11 +192,11 @@ __global__ __launch_bounds__(PNT) void k_ns_panel(const MatDesc* __restrict__ ma
     for (int ks = 0; ks < GBK / 16; ++ks)
         gfo[ks] = l32 * GKROWB + 16 * ((2 * ks + hi) ^ ((l32 >> GSH) & (GCPR - 1)));
 
-    // ---- update ring geometry (2T-byte rows of X, chunk c at c ^ 4 (r & 3)) ----
+    // ---- update ring geometry (2T-byte rows of X, chunk c at c ^ xsw(r)) ----
     // instruction q of wave w fills rows 16 q + 2 w .. +1; lane l takes
     // physical chunk l % 32 of row 2 w + l / 32
     const int uxr = wave * 2 + lane / 32;
-    const int uxc = (lane % 32) ^ (4 * (uxr & 3));
+    const int uxc = (lane % 32) ^ xsw(uxr);
     // transposing reads: lane s of 16-lane group g reads row 8 (g >> 1) + (s >> 2)
     // (+ 16 ks + 4 h), elements 32 f + 16 (g & 1) + 4 (s & 3) .. +3
     const int g16 = lane >> 4;
@@ -197,13 +206,15 @@ __global__ __launch_bounds__(PNT) void k_ns_panel(const MatDesc* __restrict__ ma
 #pragma unroll
     for (int f = 0; f < PFRJ; ++f) {
         const int e = 32 * colblk(f) + 16 * (g16 & 1) + 4 * (s16 & 3);
-        tb[f] = trow * RROW + 16 * ((e >> 3) ^ (4 * (trow & 3))) + 2 * (e & 7);
+        tb[f] = trow * RROW + 16 * ((e >> 3) ^ xsw(trow)) + 2 * (e & 7);
     }
     // a X reads: slice row l32, logical chunk 4 colblk(fj) + gq at
-    // 4 (colblk(fj) ^ (l32 & 3)) + gq, lane half hi
+    // (4 colblk(fj) + gq) ^ xsw(l32) = 4 (colblk(fj) ^ (l32 & 3)) + (gq ^ xq),
+    // lane half hi
     int xrow[PFRJ];
 #pragma unroll
     for (int f = 0; f < PFRJ; ++f) xrow[f] = l32 * RROW + 64 * (colblk(f) ^ (l32 & 3)) + 8 * hi;
+    const int xq = (l32 >> 3) & 1;
 
     const int K_g = (d.n + GBK - 1) / GBK * GBK;  // Gram K, trimmed to the valid columns
     const int nkg = K_g / GBK;                    // >= 4 (n >= m = 256)
@@ -381,7 +392,7 @@ __global__ __launch_bounds__(PNT) void k_ns_panel(const MatDesc* __restrict__ ma
                     for (int fj = 0; fj < PFRJ; ++fj)
 #pragma unroll
                         for (int gq = 0; gq < 4; ++gq) {
-                            const uint2 xv = *reinterpret_cast<const uint2*>(S + xrow[fj] + 16 * gq);
+                            const uint2 xv = *reinterpret_cast<const uint2*>(S + xrow[fj] + 16 * (gq ^ xq));
                             acc[FO][fj][4 * gq + 0] = fmaf(ca, bf16_lo(xv.x), acc[FO][fj][4 * gq + 0]);
                             acc[FO][fj][4 * gq + 1] = fmaf(ca, bf16_hi(xv.x), acc[FO][fj][4 * gq + 1]);
                             acc[FO][fj][4 * gq + 2] = fmaf(ca, bf16_lo(xv.y), acc[FO][fj][4 * gq + 2]);

@@ -84,6 +84,31 @@ def test_pmc_summary_scales_by_the_copy(tmp_path):
     assert u["hbm_bytes_per_launch"] == pytest.approx(u["fetch_bytes"] + u["write_bytes"])
 
 
+def test_lds_summary_ratios(tmp_path):
+    upd = "muon::(anonymous namespace)::k_ns_big<256, 4, 2, false, false>(x)"
+    mom = "muon::(anonymous namespace)::k_momentum<__bf16, false>(x)"
+    rows = []
+    for disp, (name, grid, vals) in enumerate((
+            (upd, 1296, {"SQ_LDS_BANK_CONFLICT": 10.0, "SQ_LDS_ADDR_CONFLICT": 2.0, "SQ_LDS_IDX_ACTIVE": 1000.0,
+                         "SQ_INSTS_LDS": 50.0}),
+            (upd, 1296, {"SQ_LDS_BANK_CONFLICT": 30.0, "SQ_LDS_ADDR_CONFLICT": 4.0, "SQ_LDS_IDX_ACTIVE": 1000.0,
+                         "SQ_INSTS_LDS": 70.0}),
+            # a smaller-grid launch (a stream group's) is not the one reported
+            (upd, 432, {"SQ_LDS_BANK_CONFLICT": 900.0, "SQ_LDS_ADDR_CONFLICT": 0.0, "SQ_LDS_IDX_ACTIVE": 1000.0,
+                        "SQ_INSTS_LDS": 1.0}),
+            (mom, 20736, {"SQ_LDS_BANK_CONFLICT": 0.0, "SQ_LDS_ADDR_CONFLICT": 0.0, "SQ_LDS_IDX_ACTIVE": 500.0,
+                          "SQ_INSTS_LDS": 8.0}))):
+        for c, v in vals.items():
+            rows.append({"Dispatch_Id": disp, "Counter_Name": c, "Kernel_Name": name, "Grid_Size": grid,
+                         "Counter_Value": v})
+    _write_csv(tmp_path / "run_counter_collection.csv", rows)
+    t = bench.lds_summary(str(tmp_path), 1)
+    u = t["kernels"]["update"]
+    assert u["dispatches"] == 2 and u["bank_conflict_pct"] == pytest.approx(2.0)
+    assert u["addr_conflict_pct"] == pytest.approx(0.3) and u["lds_insts"] == pytest.approx(60.0)
+    assert t["kernels"]["momentum"]["bank_conflict_pct"] == 0.0
+
+
 def test_cpu_baseline_leg_reports_a_rate():
     r = bench.cpu_baseline(0.5)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
